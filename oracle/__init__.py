@@ -1,0 +1,10 @@
+"""CPU float64 oracle of the GLM-5.2 MoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY: importable by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; never by the product package.
+"""
+from .moe import (Routing, bf16_bits_to_f64, decode, expert_load, expert_mlp, forward,
+                  forward_arrays, route, select_topk, sigmoid, silu, topk_gap)
+
+__all__ = ["Routing", "bf16_bits_to_f64", "decode", "expert_load", "expert_mlp", "forward",
+           "forward_arrays", "route", "select_topk", "sigmoid", "silu", "topk_gap"]

@@ -1,0 +1,166 @@
+"""CPU float64 oracle of the GLM-5.2 mixture-of-experts feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It shares no code with
+the HIP path: it decodes its own inputs, and every step is written out plainly
+in float64 NumPy, in the order the layer is stated.
+
+The layer (frontier-model-atlas "GLM-5.2 model anatomy", Feed-forward / Mixture
+of Experts panel): sigmoid router scores over 256 routed experts; an
+expert-score correction bias takes part in the top-8 selection only; the
+selected *un-biased* scores are renormalised and scaled by 2.5; the expert
+outputs are then merged with one always-on shared expert.  Expert MLPs use the
+w1 / w3 / w2 roles named on the PocketLLM "GLM-5.2" page (Implemented execution
+path): SiLU(x w1^T) * (x w3^T), then w2.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+
+* the bias is added to the post-sigmoid score, not to the logit;
+* one expert group (plain top-k over all experts);
+* renormalisation divides by the sum of the k selected un-biased scores, no eps;
+* the shared expert carries weight 1 (only routed weights are scaled);
+* ties in the biased score go to the lower expert index; slots are ordered by
+  descending biased score;
+* dropless: every (token, slot) assignment is computed.
+
+Parity pins: tests/test_oracle_pins.py (sum of weights, bias-moves-selection,
+brute-force top-k, identity-expert closed form, shared-only, invariances).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional, Sequence, Tuple
+
+import numpy as np
+
+Expert = Tuple[np.ndarray, np.ndarray, np.ndarray]
+
+
+# ----------------------------------------------------------------- decoding
+
+def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (the high half of an IEEE fp32)."""
+    u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    """float64 value of an input tensor: uint16 means bf16 bits, else its own value."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ------------------------------------------------------------------ routing
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def select_topk(beta: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest biased scores per row.
+
+    Order: descending score; equal scores keep ascending expert index (a stable
+    sort of -beta).  -0.0 and +0.0 compare equal, so they tie.
+    """
+    order = np.argsort(-beta, axis=-1, kind="stable")
+    return order[..., :k]
+
+
+@dataclasses.dataclass
+class Routing:
+    idx: np.ndarray      # [T, k] int64, slot order
+    weight: np.ndarray   # [T, k] float64
+    sigma: np.ndarray    # [T, E] un-biased sigmoid scores
+    beta: np.ndarray     # [T, E] biased scores used for selection
+
+
+def route(x, router_w, corr_bias, top_k: int, scale: float,
+          force_idx: Optional[np.ndarray] = None) -> Routing:
+    """Steps 1-4 of the layer.
+
+    1. z = x W_r^T, sigma = 1 / (1 + exp(-z))           (sigmoid router scores)
+    2. beta = sigma + b                                   (correction bias)
+    3. idx = top_k of beta, ties to the lower index       (selection)
+    4. w_j = (sigma[idx_j] / sum_i sigma[idx_i]) * scale  (un-biased renormalise, then x2.5)
+
+    ``force_idx`` replaces step 3 (used to evaluate the layer on a selection
+    that another implementation made at a near-tie); step 4 still runs.
+    """
+    x = decode(x)
+    W = decode(router_w)
+    b = decode(corr_bias)
+    z = x @ W.T
+    sigma = sigmoid(z)
+    beta = sigma + b[None, :]
+    if force_idx is None:
+        idx = select_topk(beta, top_k)
+    else:
+        idx = np.asarray(force_idx, dtype=np.int64)
+    sel = np.take_along_axis(sigma, idx, axis=1)
+    weight = (sel / sel.sum(axis=1, keepdims=True)) * scale  # renormalise, then scale
+    return Routing(idx=idx.astype(np.int64), weight=weight, sigma=sigma, beta=beta)
+
+
+def topk_gap(beta: np.ndarray, k: int) -> np.ndarray:
+    """Per-token gap between the k-th and (k+1)-th largest biased score (inf if k == E)."""
+    E = beta.shape[1]
+    if k >= E:
+        return np.full(beta.shape[0], np.inf)
+    s = -np.sort(-beta, axis=1)
+    return s[:, k - 1] - s[:, k]
+
+
+# ------------------------------------------------------------------ experts
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v / (1.0 + np.exp(-v))
+
+
+def expert_mlp(xr: np.ndarray, w1, w3, w2) -> np.ndarray:
+    """SiLU(x w1^T) * (x w3^T), then (.) w2^T; w1, w3 are [F, D], w2 is [D, F]."""
+    w1, w3, w2 = decode(w1), decode(w3), decode(w2)
+    h = silu(xr @ w1.T) * (xr @ w3.T)
+    return h @ w2.T
+
+
+def forward(x, router_w, corr_bias,
+            experts: Callable[[int], Expert],
+            shared: Expert,
+            top_k: int, scale: float,
+            force_idx: Optional[np.ndarray] = None,
+            routing: Optional[Routing] = None) -> Tuple[np.ndarray, Routing]:
+    """The whole layer: returns ``(out [T, D] float64, routing)``.
+
+    ``experts(e)`` returns routed expert e's ``(w1, w3, w2)`` (any dtype that
+    ``decode`` accepts), so the GLM-shape layer never needs all 256 experts in
+    float64 at once.
+
+    5. for every expert e: routed[t] += w[t, j] * MLP_e(x[t]) for each (t, j)
+       with idx[t, j] == e
+    6. out = routed + MLP_shared(x)                      (always-on shared expert)
+    """
+    xd = decode(x)
+    r = routing if routing is not None else route(xd, router_w, corr_bias, top_k, scale, force_idx)
+    T, D = xd.shape
+    routed = np.zeros((T, D))
+    for e in np.unique(r.idx):
+        tok, slot = np.nonzero(r.idx == e)
+        y = expert_mlp(xd[tok], *experts(int(e)))
+        routed[tok] += r.weight[tok, slot][:, None] * y
+    out = routed + expert_mlp(xd, *shared)
+    return out, r
+
+
+def forward_arrays(x, router_w, corr_bias, w1, w3, w2, sw1, sw3, sw2,
+                   top_k: int, scale: float,
+                   force_idx: Optional[np.ndarray] = None) -> Tuple[np.ndarray, Routing]:
+    """``forward`` with stacked expert tensors w1, w3 [E, F, D] and w2 [E, D, F]."""
+    return forward(x, router_w, corr_bias, lambda e: (w1[e], w3[e], w2[e]),
+                   (sw1, sw3, sw2), top_k, scale, force_idx)
+
+
+def expert_load(idx: np.ndarray, E: int) -> np.ndarray:
+    """Number of (token, slot) assignments per expert (the utilisation histogram)."""
+    return np.bincount(np.asarray(idx).reshape(-1), minlength=E)
