@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the GLM-5.2 MoE feed-forward layer on one MI355X.
+
+One step = one full layer call (router, top-k, permutation, grouped gate/up,
+grouped down, shared expert + combine) on a batch of seeded synthetic tokens
+with GLM-5.2 shapes (hidden 6144, 256 routed experts, top-8, expert width
+2048, one shared expert of width 2048, bf16 weights, fp32 router).  Weights and
+inputs are resident in HBM before timing starts.
+
+Prints one JSON line: the 8192-token prefill throughput (tokens/s) with the
+roofline of its dominant kernel, the 64-token decode step as a second record,
+and the CPU oracle timed on a bounded sample of the prefill batch.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s @GLM-5.2 shape (T=64 decode, T=8192 prefill); % roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic(w, counts):
+    """Work the method itself needs for one call, from the realised routing."""
+    T, D, E, k, F, Fs = w.T, w.D, w.E, w.k, w.F, w.Fs
+    n_active = int((counts > 0).sum())
+    wb = 2  # bf16 weight bytes
+    f = {
+        "gate_up": 2.0 * T * k * 2 * F * D + 2.0 * T * 2 * Fs * D,
+        "down": 2.0 * T * k * D * F,
+        "shared_combine": 2.0 * T * D * Fs,
+        "router_fp32": 2.0 * T * E * D,
+    }
+    b = {
+        # active experts' w1+w3, the shared w1+w3, and the input tokens
+        "gate_up": (n_active * 2 * F * D + 2 * Fs * D) * wb + T * D * 2,
+        # active experts' w2
+        "down": n_active * D * F * wb,
+        # shared w2 and the fp32 output
+        "shared_combine": D * Fs * wb + T * D * 4,
+    }
+    layer_bytes = ((n_active * 3 * F * D + 3 * Fs * D) * wb + E * D * 4 + E * 4
+                   + T * D * 2 + T * D * 4)
+    layer_flops = f["gate_up"] + f["down"] + f["shared_combine"]
+    return f, b, layer_flops, layer_bytes, n_active
+
+
+def time_layer(glm, torch, dev, w, steps, warmup, ws):
+    out = torch.empty((w.T, w.D), dtype=torch.float32, device="cuda")
+    args = dev.args()
+    for _ in range(warmup):
+        glm.forward(*args, w.k, w.scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    tr = glm.Trace(max_calls=steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        glm.forward(*args, w.k, w.scale, out=out, workspace=ws, trace=tr)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms, n = tr.read()
+    tr.close()
+    per_call = {s: v / n for s, v in stage_ms.items()}
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    glm.forward(*args, w.k, w.scale, out=out, workspace=ws, topk_idx=idx)
+    counts = torch.bincount(idx.flatten().long(), minlength=w.E).cpu().numpy()
+    return elapsed, per_call, counts
+
+
+def record(w, elapsed, steps, per_call, counts, bound):
+    f, b, lf, lb, n_active = algorithmic(w, counts)
+    ms = elapsed * 1e3 / steps
+    dom = max(("gate_up", "down", "shared_combine"), key=lambda s: per_call[s])
+    t_dom = per_call[dom] * 1e-3
+    if bound == "mfma":
+        ach = f[dom] / t_dom / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "work_per_launch": f[dom], "avg_launch_ms": round(per_call[dom], 4)}
+    else:
+        ach = b[dom] / t_dom / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "work_per_launch": b[dom], "avg_launch_ms": round(per_call[dom], 4)}
+    t_layer = ms * 1e-3
+    layer = {"tflops": round(lf / t_layer / 1e12, 2),
+             "frac_mfma": round(lf / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "hbm_gbs_algorithmic": round(lb / t_layer / 1e9, 1),
+             "frac_hbm": round(lb / t_layer / 1e9 / PEAK_HBM_GBS, 4),
+             "flops": lf, "bytes": lb}
+    load = {"active_experts": n_active, "max_rows": int(counts.max()),
+            "mean_rows": round(float(counts.mean()), 2), "min_rows": int(counts.min())}
+    return ms, roof, layer, load
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, n_tokens):
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    x = wl.make_x(w)[:n_tokens]
+    rw, cb = wl.make_router_w(w), wl.make_corr_bias(w)
+    need = np.unique(oracle.route(x, rw, cb, w.k, w.scale).idx)
+    cache = dict(wl.iter_experts(w, experts=need.tolist()))
+    shared = wl.make_shared(w)
+    t0 = time.perf_counter()
+    oracle.forward(x, rw, cb, lambda e: cache[e], shared, w.k, w.scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 4), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": (f"first {n_tokens} tokens of the {w.name} batch (T={w.T}): float64 NumPy "
+                       f"oracle, routing + the {len(need)} distinct experts they select + shared "
+                       f"expert; weights drawn before timing")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="glm_prefill")
+    ap.add_argument("--decode-workload", default="glm_decode", help="'' to skip")
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="0 to skip the oracle baseline")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this layer is built and measured on "
+              "one GPU only (no expert parallelism or collectives); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_transformer_glm_amd as glm
+    import workloads as wl
+    from workloads.device import stream_layer, to_device
+
+    torch.cuda.set_device(0)
+    wp = wl.WORKLOADS[args.workload]
+    t0 = time.time()
+    log(f"drawing + uploading {wp.name} layer weights (seeded, bf16)")
+    dev, _ = stream_layer(wp)
+    log(f"weights resident in HBM ({time.time() - t0:.1f}s)")
+
+    wd = wl.WORKLOADS[args.decode_workload] if args.decode_workload else None
+    sizes = [glm.workspace_size(wp.T, wp.D, wp.E, wp.F, wp.Fs, wp.k)]
+    if wd:
+        sizes.append(glm.workspace_size(wd.T, wd.D, wd.E, wd.F, wd.Fs, wd.k))
+    ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
+
+    elapsed, per_call, counts = time_layer(glm, torch, dev, wp, args.steps, args.warmup, ws)
+    ms, roof, layer, load = record(wp, elapsed, args.steps, per_call, counts, "mfma")
+    value = wp.T * args.steps / elapsed
+    log(f"prefill: {value:,.0f} tokens/s, {ms:.3f} ms/step, stages {per_call}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wp.name, "tokens": wp.T, "hidden": wp.D, "experts": wp.E,
+                   "top_k": wp.k, "expert_width": wp.F, "shared_width": wp.Fs,
+                   "routed_scale": wp.scale, "corr_bias_std": wp.bias_std,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "layer_roofline": layer, "routing_load": load,
+        "stages_ms": {s: round(v, 4) for s, v in per_call.items()},
+    }
+
+    if wd:
+        dd = type(dev)(wd, to_device(wl.make_x(wd)), dev.router_w,
+                       to_device(wl.make_corr_bias(wd)), dev.w1, dev.w3, dev.w2, dev.sw1,
+                       dev.sw3, dev.sw2)
+        e2, pc2, c2 = time_layer(glm, torch, dd, wd, args.decode_steps, args.warmup, ws)
+        ms2, roof2, layer2, load2 = record(wd, e2, args.decode_steps, pc2, c2, "hbm")
+        v2 = wd.T * args.decode_steps / e2
+        log(f"decode: {v2:,.0f} tokens/s, {ms2:.3f} ms/step, stages {pc2}")
+        line["decode"] = {"workload": wd.name, "tokens": wd.T, "value": round(v2, 1),
+                          "unit": "tokens/s", "steps": args.decode_steps,
+                          "ms_per_step": round(ms2, 4), "roofline": roof2,
+                          "layer_roofline": layer2, "routing_load": load2,
+                          "stages_ms": {s: round(v, 4) for s, v in pc2.items()}}
+
+    del dev
+    torch.cuda.empty_cache()
+    if args.cpu_tokens > 0:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
+        line["cpu_baseline"] = cpu_baseline(wp, args.cpu_tokens)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * glm_moe.h - C ABI of the GLM-5.2 mixture-of-experts feed-forward layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (frontier-model-atlas "GLM-5.2 model anatomy", Feed-forward /
+ * Mixture of Experts panel): a sigmoid router scores E routed experts; an
+ * expert-score correction bias takes part in the top-k selection only; the
+ * selected un-biased scores are renormalised and then scaled (2.5 for
+ * GLM-5.2); the token's expert outputs are summed with those weights and with
+ * one always-on shared expert.  Expert MLPs are SiLU-gated with the w1 (gate),
+ * w3 (up) and w2 (down) roles named on the PocketLLM "GLM-5.2" page
+ * (Implemented execution path).  GLM-5.2 sizes: hidden 6144, 256 routed
+ * experts, top-8, expert width 2048, one shared expert (PocketLLM "GLM-5.2",
+ * Model specification table).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *     allocated and owned by the caller; the library never allocates, frees
+ *     or retains device memory in route/forward.  All tensors are row-major
+ *     and contiguous, 16-byte aligned.
+ *   - Work is enqueued on `stream` and the call returns without
+ *     synchronising.  Errors in arguments are detected synchronously, before
+ *     anything is enqueued; kernel faults surface at the caller's next
+ *     synchronisation.
+ *   - No exceptions cross the ABI.  On failure the function returns a
+ *     negative glm_moe_status and glm_moe_last_error() describes the cause.
+ *   - Calls sharing one workspace must be ordered on one stream; calls with
+ *     distinct workspaces are independent.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics anywhere).
+ */
+#ifndef GLM_MOE_H
+#define GLM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define GLM_MOE_API __attribute__((visibility("default")))
+#else
+#define GLM_MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLM_MOE_OK = 0,
+  GLM_MOE_EINVAL = -1,        /* bad argument: null pointer, bad size, misalignment */
+  GLM_MOE_EUNSUPPORTED = -2,  /* valid but not implemented: E > 256, dtype mix, D or F not /64 */
+  GLM_MOE_EWORKSPACE = -3,    /* workspace_bytes smaller than glm_moe_workspace_size() */
+  GLM_MOE_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+} glm_moe_status;
+
+typedef enum {
+  GLM_MOE_F32 = 0,
+  GLM_MOE_BF16 = 1
+} glm_moe_dtype;
+
+/* Layer sizes.  T tokens, hidden D, E routed experts, routed expert width F,
+ * shared expert width F_shared.  act_dtype is the dtype of x; weight_dtype is
+ * the dtype of w1/w3/w2 and the shared expert.  Supported pairs: F32/F32 and
+ * BF16/BF16.  router_w, corr_bias, out and topk_w are always fp32. */
+typedef struct {
+  int32_t T, D, E, F, F_shared;
+  int32_t act_dtype;
+  int32_t weight_dtype;
+} glm_moe_dims;
+
+/* Workspace bytes needed by glm_moe_route / glm_moe_forward for `d` and
+ * `top_k` (written to *bytes).  Host-only; enqueues nothing.
+ * Returns GLM_MOE_OK, or EINVAL / EUNSUPPORTED for dims that route/forward
+ * would reject.  T = 0 yields 0 bytes. */
+GLM_MOE_API int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes);
+
+/* Router only: steps "sigmoid router scores", "correction bias affects top-k
+ * selection", "un-biased selected scores renormalised and scaled" of the layer
+ * statement (GLM-5.2 anatomy page, Mixture of Experts panel).
+ *   x          [T][D]   act_dtype     layer input (the normalised FFN input)
+ *   router_w   [E][D]   fp32
+ *   corr_bias  [E]      fp32          added to sigmoid scores for selection only
+ *   top_k      1 <= top_k <= min(E, 32)
+ *   scale      routed scaling factor (2.5 for GLM-5.2); any finite value
+ *   topk_idx   [T][top_k] int32  out: selected experts, slots in descending
+ *              biased score, equal scores ordered by lower expert index
+ *   topk_w     [T][top_k] fp32   out: scale * sigma_j / sum of selected sigma
+ *   workspace  device buffer of at least glm_moe_workspace_size() bytes,
+ *              256-byte aligned; contents on entry are ignored.
+ * Logits are fp32 (bf16 x is used exactly; products are exact and summed in
+ * fp32).  T = 0 is a successful no-op. */
+GLM_MOE_API int glm_moe_route(const glm_moe_dims* d, const void* x, const float* router_w,
+                  const float* corr_bias, int top_k, float scale,
+                  int32_t* topk_idx, float* topk_w,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The whole layer: routing as glm_moe_route, then every (token, slot)
+ * assignment runs through its expert (dropless), and
+ *   out[t] = sum_j topk_w[t][j] * MLP_{idx[t][j]}(x[t]) + MLP_shared(x[t]),
+ *   MLP(v) = w2 (SiLU(w1 v) * (w3 v)).
+ *   w1, w3     [E][F][D]        weight_dtype  (gate, up)
+ *   w2         [E][D][F]        weight_dtype  (down)
+ *   shared_w1, shared_w3  [F_shared][D]; shared_w2 [D][F_shared]
+ *   out        [T][D] fp32, overwritten (the residual add is not included)
+ *   topk_idx_out, topk_w_out   nullable; if given, receive the routing
+ * The bf16 path computes expert products on bf16 MFMA with fp32 accumulation
+ * and rounds the gated hidden activations to bf16; per-slot expert outputs
+ * and the final sum are fp32: the shared expert's output, then the weighted
+ * slot outputs added in slot order.
+ * The fp32 path keeps every intermediate in fp32.  T = 0 is a no-op. */
+GLM_MOE_API int glm_moe_forward(const glm_moe_dims* d, const void* x, const float* router_w,
+                    const float* corr_bias,
+                    const void* w1, const void* w3, const void* w2,
+                    const void* shared_w1, const void* shared_w3, const void* shared_w2,
+                    int top_k, float scale, float* out,
+                    int32_t* topk_idx_out, float* topk_w_out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stages of one forward call, in launch order (used by the stage trace). */
+enum {
+  GLM_MOE_STAGE_ROUTER_LOGITS = 0,
+  GLM_MOE_STAGE_ROUTER_TOPK = 1,
+  GLM_MOE_STAGE_SCAN = 2,
+  GLM_MOE_STAGE_SCATTER = 3,
+  GLM_MOE_STAGE_GATE_UP = 4,
+  GLM_MOE_STAGE_DOWN = 5,
+  GLM_MOE_STAGE_SHARED_COMBINE = 6,
+  GLM_MOE_NUM_STAGES = 7
+};
+
+/* Optional per-stage timing with HIP events recorded on the call's stream.
+ * A trace owns host-side event objects (created here, released by destroy);
+ * it records up to `max_calls` forward calls, then ignores further ones until
+ * reset.  Not thread-safe; one trace per stream. */
+typedef struct glm_moe_trace glm_moe_trace;
+GLM_MOE_API int glm_moe_trace_create(glm_moe_trace** trace, int max_calls);
+GLM_MOE_API int glm_moe_trace_destroy(glm_moe_trace* trace);
+GLM_MOE_API int glm_moe_trace_reset(glm_moe_trace* trace);
+/* Waits for the recorded events, then writes the per-stage time summed over
+ * the recorded calls (milliseconds, GLM_MOE_NUM_STAGES floats) and the number
+ * of calls recorded. */
+GLM_MOE_API int glm_moe_trace_read(glm_moe_trace* trace, float* stage_ms, int* calls);
+
+/* glm_moe_forward that also records per-stage events into `trace` (nullable:
+ * then identical to glm_moe_forward). */
+GLM_MOE_API int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* router_w,
+                           const float* corr_bias,
+                           const void* w1, const void* w3, const void* w2,
+                           const void* shared_w1, const void* shared_w3,
+                           const void* shared_w2,
+                           int top_k, float scale, float* out,
+                           int32_t* topk_idx_out, float* topk_w_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           glm_moe_trace* trace);
+
+/* Static text for a status code. */
+GLM_MOE_API const char* glm_moe_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+GLM_MOE_API const char* glm_moe_last_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+GLM_MOE_API int glm_moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLM_MOE_H */

@@ -1,0 +1,216 @@
+"""ctypes binding of ``libglm_moe.so`` (the GLM-5.2 MoE layer C ABI).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  There is no
+fallback: if the library is not built, or a tensor is not on the GPU, this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # must be imported before the library so both share one HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libglm_moe.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+STAGES = ("router_logits", "router_topk", "scan", "scatter", "gate_up", "down",
+          "shared_combine")
+
+
+class GlmMoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {detail} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("F", ctypes.c_int32), ("F_shared", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m sparse_moe_transformer_glm_amd.build` (gfx950 HIP library)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        pd = ctypes.POINTER(Dims)
+        L.glm_moe_workspace_size.argtypes = [pd, i32, ctypes.POINTER(sz)]
+        L.glm_moe_route.argtypes = [pd, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.glm_moe_forward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
+                                      vp, sz, vp]
+        L.glm_moe_forward_traced.argtypes = L.glm_moe_forward.argtypes + [vp]
+        L.glm_moe_trace_create.argtypes = [ctypes.POINTER(vp), i32]
+        L.glm_moe_trace_destroy.argtypes = [vp]
+        L.glm_moe_trace_reset.argtypes = [vp]
+        L.glm_moe_trace_read.argtypes = [vp, ctypes.POINTER(f32), ctypes.POINTER(i32)]
+        L.glm_moe_status_string.argtypes = [i32]
+        L.glm_moe_status_string.restype = ctypes.c_char_p
+        L.glm_moe_last_error.argtypes = []
+        L.glm_moe_last_error.restype = ctypes.c_char_p
+        L.glm_moe_version.restype = i32
+        for name in ("glm_moe_workspace_size", "glm_moe_route", "glm_moe_forward",
+                     "glm_moe_forward_traced", "glm_moe_trace_create", "glm_moe_trace_destroy",
+                     "glm_moe_trace_reset", "glm_moe_trace_read"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        L = lib()
+        detail = L.glm_moe_last_error().decode() or L.glm_moe_status_string(status).decode()
+        raise GlmMoeError(status, where, detail)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def dims(T: int, D: int, E: int, F: int, Fs: int, dtype: torch.dtype) -> Dims:
+    c = _dtype_code(dtype)
+    return Dims(T, D, E, F, Fs, c, c)
+
+
+def workspace_size(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
+                   dtype: torch.dtype = torch.bfloat16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().glm_moe_workspace_size(ctypes.byref(dims(T, D, E, F, Fs, dtype)), top_k,
+                                        ctypes.byref(n)), "glm_moe_workspace_size")
+    return n.value
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def new_workspace(T, D, E, F, Fs, top_k, dtype, device=None) -> torch.Tensor:
+    n = workspace_size(T, D, E, F, Fs, top_k, dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor, top_k: int,
+          scale: float, workspace: Optional[torch.Tensor] = None,
+          topk_idx: Optional[torch.Tensor] = None,
+          topk_w: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Router only; returns (topk_idx [T, k] int32, topk_w [T, k] float32)."""
+    T, D = x.shape
+    E = router_w.shape[0]
+    d = dims(T, D, E, 64, 64, x.dtype)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(T, D, E, 64, 64, top_k, x.dtype, x.device)
+    st = lib().glm_moe_route(
+        ctypes.byref(d), _ptr(x, "x"), _ptr(router_w, "router_w", torch.float32, (E, D)),
+        _ptr(corr_bias, "corr_bias", torch.float32, (E,)), top_k, float(scale),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, top_k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, top_k)),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
+    _check(st, "glm_moe_route")
+    return topk_idx, topk_w
+
+
+class Trace:
+    """Per-stage HIP event timing of forward calls on the current stream."""
+
+    def __init__(self, max_calls: int = 256):
+        h = ctypes.c_void_p()
+        _check(lib().glm_moe_trace_create(ctypes.byref(h), max_calls), "glm_moe_trace_create")
+        self.handle = h
+
+    def reset(self) -> None:
+        _check(lib().glm_moe_trace_reset(self.handle), "glm_moe_trace_reset")
+
+    def read(self) -> Tuple[dict, int]:
+        """(summed milliseconds per stage, number of calls recorded)."""
+        ms = (ctypes.c_float * len(STAGES))()
+        n = ctypes.c_int(0)
+        _check(lib().glm_moe_trace_read(self.handle, ms, ctypes.byref(n)), "glm_moe_trace_read")
+        return {s: float(ms[i]) for i, s in enumerate(STAGES)}, n.value
+
+    def close(self) -> None:
+        if self.handle:
+            lib().glm_moe_trace_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def forward(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
+            w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+            shared_w1: torch.Tensor, shared_w3: torch.Tensor, shared_w2: torch.Tensor,
+            top_k: int, scale: float, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None,
+            topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+            trace: Optional[Trace] = None) -> torch.Tensor:
+    """The whole MoE layer; returns ``out`` [T, D] float32.
+
+    Pass ``topk_idx`` / ``topk_w`` tensors to also receive the routing.
+    """
+    T, D = x.shape
+    E, F, _ = w1.shape
+    Fs = shared_w1.shape[0]
+    dt = x.dtype
+    d = dims(T, D, E, F, Fs, dt)
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(T, D, E, F, Fs, top_k, dt, x.device)
+    args = (
+        ctypes.byref(d), _ptr(x, "x", dt, (T, D)),
+        _ptr(router_w, "router_w", torch.float32, (E, D)),
+        _ptr(corr_bias, "corr_bias", torch.float32, (E,)),
+        _ptr(w1, "w1", dt, (E, F, D)), _ptr(w3, "w3", dt, (E, F, D)),
+        _ptr(w2, "w2", dt, (E, D, F)),
+        _ptr(shared_w1, "shared_w1", dt, (Fs, D)), _ptr(shared_w3, "shared_w3", dt, (Fs, D)),
+        _ptr(shared_w2, "shared_w2", dt, (D, Fs)),
+        top_k, float(scale), _ptr(out, "out", torch.float32, (T, D)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, top_k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, top_k)),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
+    L = lib()
+    if trace is None:
+        st = L.glm_moe_forward(*args)
+    else:
+        st = L.glm_moe_forward_traced(*args, trace.handle)
+    _check(st, "glm_moe_forward")
+    return out

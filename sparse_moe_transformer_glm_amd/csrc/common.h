@@ -1,0 +1,140 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code of
+// the GLM-5.2 MoE layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace glm {
+
+// ------------------------------------------------------------ vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kTokTile = 64;   // tokens per routing tile (one bit per token in a u64 mask)
+constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
+
+// Work item of a grouped GEMM launch: one BM x BN output tile of one group.
+struct TileDesc {
+  int32_t group;   // expert id; E means the shared expert
+  int32_t row0;    // first row of the tile inside the group's rows
+  int32_t rows;    // valid rows in the tile (1..BM)
+  int32_t col0;    // first output column (gate/up: first hidden column)
+};
+
+// Tile shapes chosen by the host for one grouped GEMM launch.
+struct GemmShape {
+  int BM, BN;
+};
+
+// ------------------------------------------------------- launch wrappers
+// Each returns hipGetLastError() after enqueueing on `s`.
+
+// Router logits.  partial[ks][T][E] fp32 = x[:, kslice] . router_w[:, kslice]^T.
+hipError_t launch_router_logits_bf16(const bf16_t* x, const float* router_w, float* partial,
+                                     int T, int D, int E, int ksplit, int kchunk,
+                                     hipStream_t s);
+hipError_t launch_router_logits_f32(const float* x, const float* router_w, float* partial,
+                                    int T, int D, int E, hipStream_t s);
+
+// Sum partials, sigmoid, biased top-k, renormalise and scale; per-64-token
+// tile expert membership masks.
+hipError_t launch_router_topk(const float* partial, int ksplit, const float* corr_bias,
+                              int T, int E, int k, float scale,
+                              int32_t* topk_idx, float* topk_w, uint64_t* masks,
+                              hipStream_t s);
+
+// Per-expert counts and offsets, per-(tile, expert) row bases, and the tile
+// lists of the two grouped GEMMs.
+struct ScanParams {
+  int T, E, k, F, Fs, D;
+  GemmShape gu, dn;
+  int gu_desc_cap, dn_desc_cap;
+};
+hipError_t launch_scan(const uint64_t* masks, const ScanParams& p,
+                       int32_t* counts, int32_t* offsets, int32_t* tile_base,
+                       TileDesc* gu_desc, int32_t* gu_count,
+                       TileDesc* dn_desc, int32_t* dn_count, hipStream_t s);
+
+// Stable expert-major permutation: row_assign[row] = t * k + j.
+hipError_t launch_scatter(const int32_t* topk_idx, const uint64_t* masks,
+                          const int32_t* tile_base, int T, int E, int k,
+                          int32_t* row_assign, hipStream_t s);
+
+// bf16 grouped GEMMs.
+struct GateUpArgs {
+  const bf16_t* x;             // [T][D]
+  const int32_t* row_assign;   // [T*k]
+  const int32_t* offsets;      // [E+1]
+  const bf16_t* w1;            // [E][F][D]
+  const bf16_t* w3;
+  const bf16_t* sw1;           // [Fs][D]
+  const bf16_t* sw3;
+  const TileDesc* desc;
+  const int32_t* desc_count;
+  bf16_t* H;                   // [T*k][F]
+  bf16_t* Hs;                  // [T][Fs]
+  int T, D, E, F, Fs, k;
+  int grid;                    // launched workgroups (>= desc_count, multiple of 8)
+};
+hipError_t launch_gateup_bf16(const GateUpArgs& a, GemmShape sh, hipStream_t s);
+
+struct DownArgs {
+  const bf16_t* H;             // [T*k][F]
+  const int32_t* row_assign;
+  const int32_t* offsets;
+  const bf16_t* w2;            // [E][D][F]
+  const float* topk_w;         // [T*k]
+  const TileDesc* desc;
+  const int32_t* desc_count;
+  float* Y;                    // [T*k][D]: slot outputs, already weighted
+  int T, D, E, F, k;
+  int grid;
+};
+hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s);
+
+struct CombineArgs {
+  const bf16_t* Hs;            // [T][Fs]
+  const bf16_t* sw2;           // [D][Fs]
+  const float* Y;              // [T*k][D]
+  float* out;                  // [T][D]
+  int T, D, Fs, k;
+};
+hipError_t launch_shared_combine_bf16(const CombineArgs& a, GemmShape sh, hipStream_t s);
+
+// fp32 path (plain kernels; same data flow).
+struct F32Args {
+  const float* x;
+  const int32_t* row_assign;
+  const int32_t* offsets;
+  const float* w1; const float* w3; const float* w2;
+  const float* sw1; const float* sw3; const float* sw2;
+  const float* topk_w;
+  float* H; float* Hs; float* Y; float* out;
+  int T, D, E, F, Fs, k;
+};
+hipError_t launch_gateup_f32(const F32Args& a, hipStream_t s);
+hipError_t launch_down_f32(const F32Args& a, hipStream_t s);
+hipError_t launch_shared_combine_f32(const F32Args& a, hipStream_t s);
+
+// ------------------------------------------------------------- helpers
+
+__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+__device__ inline float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ inline bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+}  // namespace glm

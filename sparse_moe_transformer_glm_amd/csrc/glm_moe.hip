@@ -1,0 +1,405 @@
+// C ABI of the GLM-5.2 MoE layer: argument checks, workspace plan and the
+// launch sequence router -> top-k -> scan -> scatter -> gate/up -> down ->
+// shared+combine, all on the caller's stream.
+#include "glm_moe.h"
+#include "common.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <vector>
+
+using namespace glm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace regions (byte offsets) and launch parameters of one call.
+struct Plan {
+  int T, D, E, F, Fs, k;
+  bool bf16;
+  int ntiles;        // 64-token routing tiles
+  int ksplit, kchunk;
+  GemmShape gu, dn, sc;
+  int gu_cap, dn_cap;
+  size_t partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
+      dn_desc, row_assign, H, Hs, Y;
+  size_t total;
+};
+
+GemmShape pick_shape(double rows_per_group) {
+  if (rows_per_group <= 16.0) return {16, 128};
+  if (rows_per_group <= 64.0) return {64, 128};
+  return {128, 128};
+}
+
+int desc_cap(int A, int E, GemmShape s, int ncol_tiles) {
+  const long nz = A < E ? A : E;
+  const long mt = ((long)A + (long)(s.BM - 1) * nz) / s.BM;
+  return (int)(mt * ncol_tiles);
+}
+
+int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
+  if (!d) return fail(GLM_MOE_EINVAL, "dims is null");
+  if (d->T < 0 || d->D <= 0 || d->E <= 0 || d->F <= 0 || d->F_shared <= 0)
+    return fail(GLM_MOE_EINVAL, "bad sizes T=%d D=%d E=%d F=%d F_shared=%d", d->T, d->D, d->E,
+                d->F, d->F_shared);
+  if (d->E > kMaxExperts)
+    return fail(GLM_MOE_EUNSUPPORTED, "E=%d exceeds %d experts", d->E, kMaxExperts);
+  const int kmax = d->E < kMaxTopK ? d->E : kMaxTopK;
+  if (top_k < 1 || top_k > kmax)
+    return fail(GLM_MOE_EINVAL, "top_k=%d outside [1, %d]", top_k, kmax);
+  if (d->act_dtype != d->weight_dtype ||
+      (d->act_dtype != GLM_MOE_F32 && d->act_dtype != GLM_MOE_BF16))
+    return fail(GLM_MOE_EUNSUPPORTED, "dtype pair act=%d weight=%d (supported: f32/f32, bf16/bf16)",
+                d->act_dtype, d->weight_dtype);
+  const bool bf16 = d->act_dtype == GLM_MOE_BF16;
+  if (bf16 && (d->D % 64 || d->F % 64 || d->F_shared % 64))
+    return fail(GLM_MOE_EUNSUPPORTED, "bf16 path needs D, F, F_shared multiples of 64 (D=%d F=%d Fs=%d)",
+                d->D, d->F, d->F_shared);
+  if ((long long)d->T * top_k > (1ll << 30))
+    return fail(GLM_MOE_EUNSUPPORTED, "T*top_k=%lld too large", (long long)d->T * top_k);
+
+  Plan& P = *p;
+  P.T = d->T; P.D = d->D; P.E = d->E; P.F = d->F; P.Fs = d->F_shared; P.k = top_k;
+  P.bf16 = bf16;
+  const int T = P.T, A = T * top_k;
+  P.ntiles = cdiv(T, kTokTile);
+
+  if (bf16) {
+    // enough (token tile, expert group, K slice) workgroups to cover the chip
+    const int base = cdiv(T, 64) * cdiv(P.E, 64);
+    int ks = cdiv(512, base > 0 ? base : 1);
+    const int ksteps = P.D / 64;
+    if (ks > 24) ks = 24;
+    if (ks > ksteps) ks = ksteps;
+    if (ks < 1) ks = 1;
+    P.kchunk = cdiv(ksteps, ks) * 64;
+    P.ksplit = cdiv(P.D, P.kchunk);
+    const double per_expert = (double)A / P.E;
+    P.gu = pick_shape(per_expert);
+    P.dn = pick_shape(per_expert);
+    P.sc = pick_shape((double)T);
+    // down and shared-combine tile the hidden width D (a multiple of 64)
+    if (P.D % 128) P.dn.BN = P.sc.BN = 64;
+    P.gu_cap = desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN) + cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
+    P.dn_cap = desc_cap(A, P.E, P.dn, P.D / P.dn.BN);
+  } else {
+    P.ksplit = 1; P.kchunk = P.D;
+    P.gu = P.dn = P.sc = GemmShape{0, 0};
+    P.gu_cap = P.dn_cap = 0;
+  }
+
+  const size_t act = bf16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  P.partial = take((size_t)P.ksplit * T * P.E * 4);
+  P.idx = take((size_t)A * 4);
+  P.w = take((size_t)A * 4);
+  P.masks = take((size_t)P.ntiles * P.E * 8);
+  P.tile_base = take((size_t)P.ntiles * P.E * 4);
+  P.counts = take((size_t)P.E * 4);
+  P.offsets = take((size_t)(P.E + 1) * 4);
+  P.gu_count = take(4);
+  P.dn_count = take(4);
+  P.gu_desc = take((size_t)P.gu_cap * sizeof(TileDesc));
+  P.dn_desc = take((size_t)P.dn_cap * sizeof(TileDesc));
+  P.row_assign = take((size_t)A * 4);
+  P.H = take((size_t)A * P.F * act);
+  P.Hs = take((size_t)T * P.Fs * act);
+  P.Y = take((size_t)A * P.D * 4);
+  P.total = T == 0 ? 0 : o;
+  return GLM_MOE_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(GLM_MOE_EINVAL, "%s is null", name);
+  if (misaligned(p)) return fail(GLM_MOE_EINVAL, "%s is not 16-byte aligned", name);
+  return GLM_MOE_OK;
+}
+
+int check_ws(const Plan& P, void* ws, size_t bytes) {
+  if (bytes < P.total)
+    return fail(GLM_MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", bytes, P.total);
+  if (!ws) return fail(GLM_MOE_EINVAL, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(GLM_MOE_EINVAL, "workspace is not %zu-byte aligned", kAlign);
+  return GLM_MOE_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+}  // namespace
+
+struct glm_moe_trace {
+  int max_calls = 0;
+  int calls = 0;
+  std::vector<hipEvent_t> ev;  // max_calls x (GLM_MOE_NUM_STAGES + 1)
+};
+
+namespace {
+
+struct Recorder {
+  glm_moe_trace* tr;
+  hipStream_t s;
+  int call;
+  explicit Recorder(glm_moe_trace* t, hipStream_t st) : tr(t), s(st), call(-1) {
+    if (tr && tr->calls < tr->max_calls) call = tr->calls++;
+  }
+  hipError_t mark(int i) {
+    if (call < 0) return hipSuccess;
+    return hipEventRecord(tr->ev[(size_t)call * (GLM_MOE_NUM_STAGES + 1) + i], s);
+  }
+};
+
+#define GLM_HIP(expr)                                                             \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess)                                                         \
+      return fail(GLM_MOE_EHIP, "%s: %s", #expr, hipGetErrorString(e_));          \
+  } while (0)
+
+int run_router(const Plan& P, const void* x, const float* router_w, const float* corr_bias,
+               float scale, int32_t* idx, float* w, void* ws, hipStream_t s, Recorder& rec) {
+  float* partial = at<float>(ws, P.partial);
+  uint64_t* masks = at<uint64_t>(ws, P.masks);
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
+  if (P.bf16)
+    GLM_HIP(launch_router_logits_bf16(static_cast<const bf16_t*>(x), router_w, partial, P.T, P.D,
+                                      P.E, P.ksplit, P.kchunk, s));
+  else
+    GLM_HIP(launch_router_logits_f32(static_cast<const float*>(x), router_w, partial, P.T, P.D,
+                                     P.E, s));
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
+  GLM_HIP(launch_router_topk(partial, P.ksplit, corr_bias, P.T, P.E, P.k, scale, idx, w, masks, s));
+  return GLM_MOE_OK;
+}
+
+int check_route_args(const void* x, const float* router_w, const float* corr_bias) {
+  int st;
+  if ((st = check_ptr(x, "x"))) return st;
+  if ((st = check_ptr(router_w, "router_w"))) return st;
+  if ((st = check_ptr(corr_bias, "corr_bias"))) return st;
+  return GLM_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes) {
+  if (!bytes) return fail(GLM_MOE_EINVAL, "bytes is null");
+  Plan P;
+  int st = make_plan(d, top_k, &P);
+  if (st) return st;
+  *bytes = P.total;
+  return GLM_MOE_OK;
+}
+
+int glm_moe_route(const glm_moe_dims* d, const void* x, const float* router_w,
+                  const float* corr_bias, int top_k, float scale, int32_t* topk_idx,
+                  float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan P;
+  int st = make_plan(d, top_k, &P);
+  if (st) return st;
+  if (P.T == 0) return GLM_MOE_OK;
+  if ((st = check_route_args(x, router_w, corr_bias))) return st;
+  if ((st = check_ptr(topk_idx, "topk_idx"))) return st;
+  if ((st = check_ptr(topk_w, "topk_w"))) return st;
+  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+  Recorder rec(nullptr, stream);
+  return run_router(P, x, router_w, corr_bias, scale, topk_idx, topk_w, workspace, stream, rec);
+}
+
+int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* router_w,
+                           const float* corr_bias, const void* w1, const void* w3,
+                           const void* w2, const void* shared_w1, const void* shared_w3,
+                           const void* shared_w2, int top_k, float scale, float* out,
+                           int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, glm_moe_trace* trace) {
+  Plan P;
+  int st = make_plan(d, top_k, &P);
+  if (st) return st;
+  if (P.T == 0) return GLM_MOE_OK;
+  if ((st = check_route_args(x, router_w, corr_bias))) return st;
+  if ((st = check_ptr(w1, "w1")) || (st = check_ptr(w3, "w3")) || (st = check_ptr(w2, "w2")) ||
+      (st = check_ptr(shared_w1, "shared_w1")) || (st = check_ptr(shared_w3, "shared_w3")) ||
+      (st = check_ptr(shared_w2, "shared_w2")) || (st = check_ptr(out, "out")))
+    return st;
+  if (topk_idx_out && misaligned(topk_idx_out))
+    return fail(GLM_MOE_EINVAL, "topk_idx_out is not 16-byte aligned");
+  if (topk_w_out && misaligned(topk_w_out))
+    return fail(GLM_MOE_EINVAL, "topk_w_out is not 16-byte aligned");
+  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+
+  void* ws = workspace;
+  hipStream_t s = stream;
+  Recorder rec(trace, s);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, P.idx);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, P.w);
+  if ((st = run_router(P, x, router_w, corr_bias, scale, idx, wts, ws, s, rec))) return st;
+
+  uint64_t* masks = at<uint64_t>(ws, P.masks);
+  int32_t* tile_base = at<int32_t>(ws, P.tile_base);
+  int32_t* counts = at<int32_t>(ws, P.counts);
+  int32_t* offsets = at<int32_t>(ws, P.offsets);
+  int32_t* gu_count = at<int32_t>(ws, P.gu_count);
+  int32_t* dn_count = at<int32_t>(ws, P.dn_count);
+  TileDesc* gu_desc = at<TileDesc>(ws, P.gu_desc);
+  TileDesc* dn_desc = at<TileDesc>(ws, P.dn_desc);
+  int32_t* row_assign = at<int32_t>(ws, P.row_assign);
+  float* Y = at<float>(ws, P.Y);
+
+  ScanParams sp;
+  sp.T = P.T; sp.E = P.E; sp.k = P.k; sp.F = P.F; sp.Fs = P.Fs; sp.D = P.D;
+  // the fp32 path does not use the tile lists; give the scan a harmless shape
+  sp.gu = P.bf16 ? P.gu : GemmShape{16, 128};
+  sp.dn = P.bf16 ? P.dn : GemmShape{16, 128};
+  sp.gu_desc_cap = P.gu_cap;
+  sp.dn_desc_cap = P.dn_cap;
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_SCAN));
+  GLM_HIP(launch_scan(masks, sp, counts, offsets, tile_base, gu_desc, gu_count, dn_desc, dn_count, s));
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));
+  GLM_HIP(launch_scatter(idx, masks, tile_base, P.T, P.E, P.k, row_assign, s));
+
+  if (P.bf16) {
+    GateUpArgs ga{};
+    ga.x = static_cast<const bf16_t*>(x);
+    ga.row_assign = row_assign; ga.offsets = offsets;
+    ga.w1 = static_cast<const bf16_t*>(w1); ga.w3 = static_cast<const bf16_t*>(w3);
+    ga.sw1 = static_cast<const bf16_t*>(shared_w1); ga.sw3 = static_cast<const bf16_t*>(shared_w3);
+    ga.desc = gu_desc; ga.desc_count = gu_count;
+    ga.H = at<bf16_t>(ws, P.H); ga.Hs = at<bf16_t>(ws, P.Hs);
+    ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
+    ga.grid = cdiv(P.gu_cap, kXcds) * kXcds;
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
+    GLM_HIP(launch_gateup_bf16(ga, P.gu, s));
+
+    DownArgs da{};
+    da.H = ga.H; da.row_assign = row_assign; da.offsets = offsets;
+    da.w2 = static_cast<const bf16_t*>(w2); da.topk_w = wts;
+    da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
+    da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.k = P.k;
+    da.grid = cdiv(P.dn_cap, kXcds) * kXcds;
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
+    GLM_HIP(launch_down_bf16(da, P.dn, s));
+
+    CombineArgs ca{};
+    ca.Hs = ga.Hs; ca.sw2 = static_cast<const bf16_t*>(shared_w2); ca.Y = Y; ca.out = out;
+    ca.T = P.T; ca.D = P.D; ca.Fs = P.Fs; ca.k = P.k;
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_SHARED_COMBINE));
+    GLM_HIP(launch_shared_combine_bf16(ca, P.sc, s));
+  } else {
+    F32Args fa{};
+    fa.x = static_cast<const float*>(x);
+    fa.row_assign = row_assign; fa.offsets = offsets;
+    fa.w1 = static_cast<const float*>(w1); fa.w3 = static_cast<const float*>(w3);
+    fa.w2 = static_cast<const float*>(w2);
+    fa.sw1 = static_cast<const float*>(shared_w1); fa.sw3 = static_cast<const float*>(shared_w3);
+    fa.sw2 = static_cast<const float*>(shared_w2);
+    fa.topk_w = wts;
+    fa.H = at<float>(ws, P.H); fa.Hs = at<float>(ws, P.Hs); fa.Y = Y; fa.out = out;
+    fa.T = P.T; fa.D = P.D; fa.E = P.E; fa.F = P.F; fa.Fs = P.Fs; fa.k = P.k;
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
+    GLM_HIP(launch_gateup_f32(fa, s));
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
+    GLM_HIP(launch_down_f32(fa, s));
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_SHARED_COMBINE));
+    GLM_HIP(launch_shared_combine_f32(fa, s));
+  }
+  GLM_HIP(rec.mark(GLM_MOE_NUM_STAGES));
+  return GLM_MOE_OK;
+}
+
+int glm_moe_forward(const glm_moe_dims* d, const void* x, const float* router_w,
+                    const float* corr_bias, const void* w1, const void* w3, const void* w2,
+                    const void* shared_w1, const void* shared_w3, const void* shared_w2,
+                    int top_k, float scale, float* out, int32_t* topk_idx_out,
+                    float* topk_w_out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return glm_moe_forward_traced(d, x, router_w, corr_bias, w1, w3, w2, shared_w1, shared_w3,
+                                shared_w2, top_k, scale, out, topk_idx_out, topk_w_out,
+                                workspace, workspace_bytes, stream, nullptr);
+}
+
+int glm_moe_trace_create(glm_moe_trace** trace, int max_calls) {
+  if (!trace) return fail(GLM_MOE_EINVAL, "trace is null");
+  if (max_calls < 1) return fail(GLM_MOE_EINVAL, "max_calls=%d < 1", max_calls);
+  glm_moe_trace* t = new (std::nothrow) glm_moe_trace;
+  if (!t) return fail(GLM_MOE_EINVAL, "out of host memory");
+  t->max_calls = max_calls;
+  t->ev.assign((size_t)max_calls * (GLM_MOE_NUM_STAGES + 1), nullptr);
+  for (auto& e : t->ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      glm_moe_trace_destroy(t);
+      return fail(GLM_MOE_EHIP, "hipEventCreate: %s", hipGetErrorString(r));
+    }
+  }
+  *trace = t;
+  return GLM_MOE_OK;
+}
+
+int glm_moe_trace_destroy(glm_moe_trace* trace) {
+  if (!trace) return GLM_MOE_OK;
+  for (auto& e : trace->ev)
+    if (e) (void)hipEventDestroy(e);
+  delete trace;
+  return GLM_MOE_OK;
+}
+
+int glm_moe_trace_reset(glm_moe_trace* trace) {
+  if (!trace) return fail(GLM_MOE_EINVAL, "trace is null");
+  trace->calls = 0;
+  return GLM_MOE_OK;
+}
+
+int glm_moe_trace_read(glm_moe_trace* trace, float* stage_ms, int* calls) {
+  if (!trace || !stage_ms || !calls) return fail(GLM_MOE_EINVAL, "null argument");
+  for (int s = 0; s < GLM_MOE_NUM_STAGES; ++s) stage_ms[s] = 0.f;
+  const int n = GLM_MOE_NUM_STAGES + 1;
+  for (int c = 0; c < trace->calls; ++c) {
+    hipEvent_t* ev = &trace->ev[(size_t)c * n];
+    hipError_t r = hipEventSynchronize(ev[n - 1]);
+    if (r != hipSuccess) return fail(GLM_MOE_EHIP, "hipEventSynchronize: %s", hipGetErrorString(r));
+    for (int s = 0; s < GLM_MOE_NUM_STAGES; ++s) {
+      float ms = 0.f;
+      r = hipEventElapsedTime(&ms, ev[s], ev[s + 1]);
+      if (r != hipSuccess) return fail(GLM_MOE_EHIP, "hipEventElapsedTime: %s", hipGetErrorString(r));
+      stage_ms[s] += ms;
+    }
+  }
+  *calls = trace->calls;
+  return GLM_MOE_OK;
+}
+
+const char* glm_moe_status_string(int status) {
+  switch (status) {
+    case GLM_MOE_OK: return "ok";
+    case GLM_MOE_EINVAL: return "invalid argument";
+    case GLM_MOE_EUNSUPPORTED: return "unsupported configuration";
+    case GLM_MOE_EWORKSPACE: return "workspace too small";
+    case GLM_MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* glm_moe_last_error(void) { return g_err; }
+
+int glm_moe_version(void) { return 100; }
+
+}  // extern "C"

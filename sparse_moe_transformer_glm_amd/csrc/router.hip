@@ -1,0 +1,213 @@
+// Router of the GLM-5.2 MoE layer: sigmoid scores, bias-adjusted top-k
+// selection, un-biased renormalisation and scaling (frontier-model-atlas
+// "GLM-5.2 model anatomy", Feed-forward / Mixture of Experts panel).
+#include "common.h"
+
+namespace glm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Split 8 fp32 values into three bf16 vectors with w == hi + mid + lo exactly
+// (each remainder has at most 16, then 8, significant bits).
+__device__ inline void split3(const float4 w0, const float4 w1, bf16x8& hi, bf16x8& mid,
+                              bf16x8& lo) {
+  float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    bf16_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float a = v[i + j];
+      hb[j] = f32_to_bf16(a);
+      float r1 = a - bf16_to_f32(hb[j]);
+      mb[j] = f32_to_bf16(r1);
+      float r2 = r1 - bf16_to_f32(mb[j]);
+      lb[j] = f32_to_bf16(r2);
+    }
+    h[i / 2] = hb[0] | (uint32_t(hb[1]) << 16);
+    m[i / 2] = mb[0] | (uint32_t(mb[1]) << 16);
+    l[i / 2] = lb[0] | (uint32_t(lb[1]) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+  mid = __builtin_bit_cast(bf16x8, (u32x4){m[0], m[1], m[2], m[3]});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+}
+
+// One workgroup: 64 tokens x 64 experts over one K slice.  Wave w owns experts
+// [16w, 16w+16) of the group and all 64 tokens (four 16-row MFMA blocks).
+// MFMA 16x16x32 bf16: lane l supplies row (l % 16), k-group (l / 16) of both
+// operands; the accumulator holds rows 4*(l/16)+r, column l % 16.
+__global__ __launch_bounds__(256) void router_logits_bf16_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
+    int T, int D, int E, int kchunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int t0 = blockIdx.x * 64;
+  const int e0 = blockIdx.y * 64 + wave * 16;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * kchunk;
+  const int kend = min(D, kbeg + kchunk);
+
+  const float* wrow = W + (size_t)min(e0 + r16, E - 1) * D;
+  const bf16_t* xrow[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) xrow[m] = x + (size_t)min(t0 + 16 * m + r16, T - 1) * D;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int k = kbeg; k < kend; k += 32) {
+    const int kk = k + kg * 8;
+    const float4 w0 = *reinterpret_cast<const float4*>(wrow + kk);
+    const float4 w1 = *reinterpret_cast<const float4*>(wrow + kk + 4);
+    bf16x8 a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const bf16x8*>(xrow[m] + kk);
+    bf16x8 hi, mid, lo;
+    split3(w0, w1, hi, mid, lo);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], lo, acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], mid, acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], hi, acc[m], 0, 0, 0);
+    }
+  }
+
+  const int e = e0 + r16;
+  if (e >= E) return;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * m + 4 * kg + r;
+      if (t < T) partial[((size_t)ks * T + t) * E + e] = acc[m][r];
+    }
+  }
+}
+
+// fp32 activations: plain fp32 dot products, one thread per (token, expert).
+__global__ __launch_bounds__(256) void router_logits_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
+    int T, int D, int E) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * E) return;
+  const int t = (int)(i / E), e = (int)(i % E);
+  const float* xr = x + (size_t)t * D;
+  const float* wr = W + (size_t)e * D;
+  float acc = 0.f;
+  for (int d = 0; d < D; ++d) acc = fmaf(xr[d], wr[d], acc);
+  partial[i] = acc;
+}
+
+// Order-preserving map of a float to an unsigned integer (larger float, larger key).
+__device__ inline uint32_t ordered_bits(float f) {
+  if (f == 0.0f) f = 0.0f;  // -0 and +0 tie
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One workgroup per 64-token tile, four waves, one wave per token at a time.
+// Lane l holds experts l, l+64, l+128, l+192.  Selection takes k rounds of a
+// wave-wide max over 64-bit keys (biased score, then lower index).
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float* __restrict__ partial, int ksplit, const float* __restrict__ bias,
+    int T, int E, int k, float scale, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out, uint64_t* __restrict__ masks) {
+  __shared__ unsigned long long smask[kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  smask[threadIdx.x] = 0ull;
+  __syncthreads();
+
+  const int tile = blockIdx.x;
+  float b[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    b[c] = e < E ? bias[e] : 0.f;
+  }
+
+  for (int i = 0; i < 16; ++i) {
+    const int tl = wave * 16 + i;
+    const int t = tile * kTokTile + tl;
+    if (t >= T) break;
+    float sig[4];
+    unsigned long long key[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      sig[c] = 0.f;
+      key[c] = 0ull;
+      if (e < E) {
+        float z = 0.f;
+        for (int s = 0; s < ksplit; ++s) z += partial[((size_t)s * T + t) * E + e];
+        const float sg = 1.0f / (1.0f + expf(-z));
+        sig[c] = sg;
+        key[c] = ((unsigned long long)ordered_bits(sg + b[c]) << 32) | (uint32_t)(~e);
+      }
+    }
+    float ssum = 0.f, my_sig = 0.f;
+    int my_e = -1;
+    for (int j = 0; j < k; ++j) {
+      unsigned long long best = key[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, 64);
+        best = o > best ? o : best;
+      }
+      const int es = (int)(~(uint32_t)best);
+      const int src = es & 63, cs = es >> 6;
+      float mine = sig[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) mine = (cs == c) ? sig[c] : mine;
+      const float ss = __shfl(mine, src, 64);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (lane == src && cs == c) key[c] = 0ull;
+      ssum += ss;
+      if (lane == j) {
+        my_e = es;
+        my_sig = ss;
+      }
+      if (lane == 0) atomicOr(&smask[es], 1ull << tl);
+    }
+    if (lane < k) {
+      idx_out[(size_t)t * k + lane] = my_e;
+      w_out[(size_t)t * k + lane] = (my_sig / ssum) * scale;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < E) masks[(size_t)tile * E + threadIdx.x] = smask[threadIdx.x];
+}
+
+}  // namespace
+
+hipError_t launch_router_logits_bf16(const bf16_t* x, const float* router_w, float* partial,
+                                     int T, int D, int E, int ksplit, int kchunk,
+                                     hipStream_t s) {
+  dim3 grid(cdiv(T, 64), cdiv(E, 64), ksplit);
+  router_logits_bf16_kernel<<<grid, 256, 0, s>>>(x, router_w, partial, T, D, E, kchunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits_f32(const float* x, const float* router_w, float* partial,
+                                    int T, int D, int E, hipStream_t s) {
+  const size_t n = (size_t)T * E;
+  router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, router_w, partial,
+                                                                         T, D, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float* partial, int ksplit, const float* corr_bias, int T,
+                              int E, int k, float scale, int32_t* topk_idx, float* topk_w,
+                              uint64_t* masks, hipStream_t s) {
+  router_topk_kernel<<<cdiv(T, kTokTile), 256, 0, s>>>(partial, ksplit, corr_bias, T, E, k,
+                                                        scale, topk_idx, topk_w, masks);
+  return hipGetLastError();
+}
+
+}  // namespace glm

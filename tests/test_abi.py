@@ -1,0 +1,162 @@
+"""C ABI: the library loads, exports every declared symbol, and validates
+arguments on the host (no GPU work is enqueued by any call here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_moe_transformer_glm_amd as glm
+from sparse_moe_transformer_glm_amd._lib import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "glm_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(glm_moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("glm_moe_route", "glm_moe_forward", "glm_moe_workspace_size",
+              "glm_moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", glm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (glm_moe_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    L = glm.lib()
+    for n in declared_functions():
+        assert getattr(L, n) is not None
+
+
+def test_exports_are_c_linkage_only():
+    out = subprocess.run(["nm", "-D", "--defined-only", glm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = re.findall(r"\bT (\S+)", out)
+    assert [s for s in text_syms if s.startswith("glm_moe_")]
+    assert not [s for s in text_syms if "glm" in s and not s.startswith("glm_moe_")], \
+        "internal symbols are exported"
+
+
+def _ws(T, D, E, F, Fs, k, dt=glm.BF16):
+    n = ctypes.c_size_t(0)
+    st = glm.lib().glm_moe_workspace_size(ctypes.byref(Dims(T, D, E, F, Fs, dt, dt)), k,
+                                          ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    st, n0 = _ws(0, 6144, 256, 2048, 2048, 8)
+    assert st == glm.OK and n0 == 0
+    st, n1 = _ws(64, 6144, 256, 2048, 2048, 8)
+    assert st == glm.OK
+    # at least the fp32 slot outputs and the bf16 hidden activations
+    assert n1 >= 64 * 8 * 6144 * 4 + 64 * 8 * 2048 * 2
+    st, n2 = _ws(8192, 6144, 256, 2048, 2048, 8)
+    assert st == glm.OK and n2 > n1
+    st, n3 = _ws(64, 128, 8, 64, 64, 2, glm.F32)
+    assert st == glm.OK and n3 > 0
+    assert n2 % 256 == 0
+
+
+@pytest.mark.parametrize("dims,k,code", [
+    ((64, 6144, 257, 2048, 2048), 8, glm.EUNSUPPORTED),   # E > 256
+    ((64, 6144, 256, 2048, 2048), 0, glm.EINVAL),         # top_k < 1
+    ((64, 6144, 256, 2048, 2048), 33, glm.EINVAL),        # top_k > 32
+    ((64, 128, 4, 64, 64), 5, glm.EINVAL),                # top_k > E
+    ((64, 100, 8, 64, 64), 2, glm.EUNSUPPORTED),          # bf16 D not /64
+    ((64, 128, 8, 96, 64), 2, glm.EUNSUPPORTED),          # bf16 F not /64
+    ((64, 128, 8, 64, 32), 2, glm.EUNSUPPORTED),          # bf16 F_shared not /64
+    ((-1, 128, 8, 64, 64), 2, glm.EINVAL),                # negative T
+    ((64, 0, 8, 64, 64), 2, glm.EINVAL),                  # D = 0
+])
+def test_invalid_dims(dims, k, code):
+    st, _ = _ws(*dims, k)
+    assert st == code
+    assert glm.lib().glm_moe_last_error()
+
+
+def test_dtype_mix_unsupported():
+    n = ctypes.c_size_t(0)
+    st = glm.lib().glm_moe_workspace_size(ctypes.byref(Dims(64, 128, 8, 64, 64, glm.BF16, glm.F32)),
+                                          2, ctypes.byref(n))
+    assert st == glm.EUNSUPPORTED
+
+
+def test_fp32_path_accepts_any_sizes():
+    st, n = _ws(5, 100, 3, 30, 7, 2, glm.F32)
+    assert st == glm.OK and n > 0
+
+
+def _forward(d, k, ptrs, ws=0, ws_bytes=0):
+    L = glm.lib()
+    return L.glm_moe_forward(ctypes.byref(d), *ptrs[:9], k, 2.5, ptrs[9], None, None, ws,
+                             ws_bytes, None)
+
+
+FAKE = 1 << 40  # never dereferenced: validation fails before any enqueue
+
+
+def test_forward_null_and_alignment_checks():
+    d = Dims(64, 128, 8, 64, 64, glm.BF16, glm.BF16)
+    good = [FAKE] * 10
+    for i in range(10):
+        p = list(good)
+        p[i] = 0
+        assert _forward(d, 2, p) == glm.EINVAL
+    for i in range(10):
+        p = list(good)
+        p[i] = FAKE + 8
+        assert _forward(d, 2, p) == glm.EINVAL
+
+
+def test_forward_workspace_checks():
+    d = Dims(64, 128, 8, 64, 64, glm.BF16, glm.BF16)
+    _, need = _ws(64, 128, 8, 64, 64, 2)
+    good = [FAKE] * 10
+    assert _forward(d, 2, good, FAKE, need - 1) == glm.EWORKSPACE
+    assert _forward(d, 2, good, 0, need) == glm.EINVAL
+    assert _forward(d, 2, good, FAKE + 16, need) == glm.EINVAL  # not 256-byte aligned
+
+
+def test_zero_tokens_is_a_no_op():
+    d = Dims(0, 128, 8, 64, 64, glm.BF16, glm.BF16)
+    assert _forward(d, 2, [0] * 10) == glm.OK
+    L = glm.lib()
+    assert L.glm_moe_route(ctypes.byref(d), None, None, None, 2, 2.5, None, None, None, 0,
+                           None) == glm.OK
+
+
+def test_route_validation():
+    L = glm.lib()
+    d = Dims(64, 128, 8, 64, 64, glm.BF16, glm.BF16)
+    assert L.glm_moe_route(ctypes.byref(d), FAKE, FAKE, FAKE, 9, 2.5, FAKE, FAKE, FAKE, 1 << 30,
+                           None) == glm.EINVAL
+    assert L.glm_moe_route(None, FAKE, FAKE, FAKE, 2, 2.5, FAKE, FAKE, FAKE, 1 << 30,
+                           None) == glm.EINVAL
+
+
+def test_status_strings_and_version():
+    L = glm.lib()
+    for code in (glm.OK, glm.EINVAL, glm.EUNSUPPORTED, glm.EWORKSPACE, glm.EHIP):
+        assert L.glm_moe_status_string(code)
+    assert L.glm_moe_status_string(12345) == b"unknown status"
+    assert L.glm_moe_version() >= 100
+
+
+def test_trace_argument_checks():
+    L = glm.lib()
+    assert L.glm_moe_trace_create(None, 4) == glm.EINVAL
+    h = ctypes.c_void_p()
+    assert L.glm_moe_trace_create(ctypes.byref(h), 0) == glm.EINVAL
+    assert L.glm_moe_trace_reset(None) == glm.EINVAL
+    assert L.glm_moe_trace_destroy(None) == glm.OK
