@@ -191,11 +191,15 @@ def test_identity_experts_closed_form():
         coef = sum(wt[t, j] * (idx[t, j] + 1.0) for j in range(k)) + 1.0
         g = x[t, :F]
         want[t, perm] = coef * (g / (1.0 + np.exp(-g))) * (2.0 * g)
-    o = parity.compare_output(out, want)
-    assert o.max_rel <= parity.BF16_MAX_REL and o.mean_rel <= parity.BF16_MEAN_REL
+    # Every weight here is exact in bf16, so the only lossy step is the bf16
+    # rounding of the gated hidden value (relative 2^-9); each output element
+    # is one such value times fp32 factors.
+    err = np.abs(out - want)
+    assert (err <= 2.0 ** -8 * np.abs(want) + 1e-6).all(), err.max()
     rows = np.setdiff1d(np.arange(D), perm)
     assert (out[:, rows] == 0).all()
-    check(L, out, idx, wt, label="identity")
+    rep = parity.compare_routing(idx, wt, L.x, L.router_w, L.corr_bias, k, w.scale)
+    assert rep.ok and rep.max_weight_err <= parity.WEIGHT_TOL
 
 
 def test_zero_tokens_leaves_output_untouched():
