@@ -36,11 +36,12 @@ struct GemmShape {
 // Each returns hipGetLastError() after enqueueing on `s`.
 
 // Router logits.  partial[ks][T][E] fp32 = x[:, kslice] . router_w[:, kslice]^T.
+// Both also clear masks[ceil(T/64)][E] for the top-k kernel.
 hipError_t launch_router_logits_bf16(const bf16_t* x, const float* router_w, float* partial,
                                      int T, int D, int E, int ksplit, int kchunk,
-                                     hipStream_t s);
+                                     uint64_t* masks, hipStream_t s);
 hipError_t launch_router_logits_f32(const float* x, const float* router_w, float* partial,
-                                    int T, int D, int E, hipStream_t s);
+                                    int T, int D, int E, uint64_t* masks, hipStream_t s);
 
 // Sum partials, sigmoid, biased top-k, renormalise and scale; per-64-token
 // tile expert membership masks.
@@ -82,30 +83,32 @@ struct GateUpArgs {
   int T, D, E, F, Fs, k;
   int grid;                    // launched workgroups (>= desc_count, multiple of 8)
 };
+// Tile shape of a grouped GEMM launch.  `wide` says the output width allows
+// the 256-column tiles (gate/up: F and F_shared multiples of 128; down and
+// shared-combine: D a multiple of 256); otherwise 64-column tiles are used.
+GemmShape gemm_shape(double rows_per_group, bool wide);
+
 hipError_t launch_gateup_bf16(const GateUpArgs& a, GemmShape sh, hipStream_t s);
 
 struct DownArgs {
   const bf16_t* H;             // [T*k][F]
+  const bf16_t* Hs;            // [T][Fs]
   const int32_t* row_assign;
   const int32_t* offsets;
   const bf16_t* w2;            // [E][D][F]
+  const bf16_t* sw2;           // [D][Fs]
   const float* topk_w;         // [T*k]
-  const TileDesc* desc;
+  const TileDesc* desc;        // routed groups, then the shared expert (group E)
   const int32_t* desc_count;
-  float* Y;                    // [T*k][D]: slot outputs, already weighted
-  int T, D, E, F, k;
+  float* Y;                    // [T][k+1][D]: slot j < k routed (weighted), slot k shared
+  int T, D, E, F, Fs, k;
   int grid;
 };
 hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s);
 
-struct CombineArgs {
-  const bf16_t* Hs;            // [T][Fs]
-  const bf16_t* sw2;           // [D][Fs]
-  const float* Y;              // [T*k][D]
-  float* out;                  // [T][D]
-  int T, D, Fs, k;
-};
-hipError_t launch_shared_combine_bf16(const CombineArgs& a, GemmShape sh, hipStream_t s);
+// out[t] = Y[t][k] + sum_{j<k} Y[t][j]: the shared expert's output, then the
+// weighted routed outputs in slot order.
+hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, hipStream_t s);
 
 // fp32 path (plain kernels; same data flow).
 struct F32Args {
@@ -121,6 +124,9 @@ struct F32Args {
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_down_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_shared_combine_f32(const F32Args& a, hipStream_t s);
+
+// Row of Y holding assignment a = t * k + j (slot j of token t).
+__host__ __device__ inline int y_row(int a, int k) { return (a / k) * (k + 1) + a % k; }
 
 // ------------------------------------------------------------- helpers
 

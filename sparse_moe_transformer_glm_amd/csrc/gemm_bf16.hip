@@ -1,50 +1,87 @@
 // Grouped expert GEMMs of the GLM-5.2 MoE layer on gfx950 bf16 MFMA.
 //
 // Every product here is C[M x N] = A[M x K] . B[N x K]^T with both operands
-// K-contiguous: A rows are token activations (gathered) or gated hidden rows,
-// B rows are weight rows (w1/w3 [F][D], w2 [D][F]).  One workgroup computes a
-// BM x BN tile: K is walked in steps of 64 through double-buffered LDS tiles
-// (rows padded by 16 bytes so the MFMA fragment reads are conflict-free), and
-// each wave accumulates a (BM/WM) x (BN/WN) sub-tile with
-// v_mfma_f32_16x16x32_bf16.
+// K-contiguous: A rows are token activations (gathered through the
+// permutation) or gated hidden rows, B rows are weight rows (w1/w3 [F][D],
+// w2 [D][F]).  One workgroup computes a BM x BN tile.
 //
-// Three epilogues:
-//  * GATE_UP: B-tile rows alternate 16 rows of w1 (gate) and the matching 16
+// Data movement: K is walked in steps of BK through a ring of ST LDS stages,
+// each a separate LDS object.  Tiles are copied global -> LDS with gfx950's
+// 16-byte LDS-DMA loads (no staging registers), ST-1 steps ahead of the MFMA
+// work, and each wave waits only for the oldest stage (vmcnt), so HBM latency
+// is covered by up to ST-1 steps of math.  Rows are stored unpadded with the
+// 16-byte chunks of each row XOR-swizzled, which keeps the MFMA fragment reads
+// free of bank conflicts.
+//
+// Math: each wave owns a (BM/WM) x (BN/WN) sub-tile and accumulates it with
+// v_mfma_f32_32x32x16_bf16 (MB = 32) or v_mfma_f32_16x16x32_bf16 (MB = 16).
+// The valid rows of a partial tile are split evenly between the wave rows and
+// MFMA blocks holding no valid row are skipped.
+//
+// Epilogues:
+//  * GATE_UP: B-tile rows alternate MB rows of w1 (gate) with the matching MB
 //    rows of w3 (up), so one lane holds gate and up of the same hidden unit and
-//    writes H = bf16(SiLU(g) * u)  (SiLU-gated expert MLP; w1/w3/w2 roles as on
-//    the PocketLLM "GLM-5.2" page, Implemented execution path).
-//  * DOWN: Y[t*k+j] = w[t][j] * (H W2^T): the routing weight is applied and the
-//    row is written straight to its (token, slot) place (un-permute); no atomics.
-//  * SHARED_COMBINE: out[t] = Hs[t] Ws2^T + sum_j Y[t*k+j] in slot order: the
-//    always-on shared expert merged with the weighted routed outputs
-//    (GLM-5.2 anatomy page, Mixture of Experts panel).
+//    writes H = bf16(SiLU(g) * u) (SiLU-gated expert MLP with the w1/w3/w2 roles
+//    of the PocketLLM "GLM-5.2" page, Implemented execution path).
+//  * DOWN: Y[t][j] = w[t][j] * (H W2^T): the routing weight is applied and the
+//    row lands in its (token, slot) place (un-permute); no atomics.  The
+//    shared expert is the last group and writes Y[t][k] with weight 1.
+// A streaming kernel then forms out[t] = Y[t][k] + sum_j Y[t][j] in slot
+// order: the always-on shared expert merged with the weighted routed outputs
+// (GLM-5.2 anatomy page, Mixture of Experts panel).
 #include "common.h"
 
+#include <type_traits>
+
 namespace glm {
-namespace {
+// Named (not anonymous) so the host launch stubs of the kernel template are
+// emitted; the library exports only the C ABI.
+namespace gemm {
 
-enum Mode { GATE_UP = 0, DOWN = 1, SHARED_COMBINE = 2 };
+enum Mode { GATE_UP = 0, DOWN = 1 };
 
-constexpr int BK = 64;          // K step (bf16 elements) = 8 chunks of 16 bytes
-constexpr int LDK = BK + 8;     // padded LDS row (elements)
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int WM, int WN>
-struct Tile {
-  static constexpr int NT = WM * WN * kWave;
+// s_waitcnt immediate: vector-memory count N, other counters left alone.
+#define GLM_VMCNT(N) (((N) & 0xF) | (((N) >> 4) << 14) | (7 << 4) | (0xF << 8))
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Physical 16-byte chunk of logical chunk c in row r: c ^ swz(r).  Rows r and
+// r+1..r+15 read at one logical chunk land on distinct banks for both 8- and
+// 16-lane LDS phases.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int ST_, int MB_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, ST = ST_, MB = MB_;
+  static constexpr int NW = WM * WN, NT = NW * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;
-  static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int A_CHUNKS = BM * (BK / 8), B_CHUNKS = BN * (BK / 8);
-  static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
-  static constexpr int B_PER = (B_CHUNKS + NT - 1) / NT;
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  static constexpr int FM = TM / MB, FN = TN / MB;
+  static constexpr int CPR = BK / 8;          // 16-byte chunks per row
+  static constexpr int RPI = kWave / CPR;     // rows per DMA instruction (1 KB)
+  static constexpr int A_INST = BM / RPI, B_INST = BN / RPI;
+  static constexpr int IPW = (A_INST + B_INST) / NW;  // DMA instructions per wave per stage
+  static constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
+  static constexpr int KSUB = BK / (MB == 32 ? 16 : 32);  // MFMA k-steps per stage
+  static_assert(TM % MB == 0 && TN % MB == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles must be whole DMA instructions");
+  static_assert((A_INST + B_INST) % NW == 0, "every wave issues the same number of DMAs");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
 };
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Maps a workgroup to a logical tile index.  Logical tiles are split into 8
-// contiguous chunks, one per XCD (workgroups are dispatched round-robin over
-// the XCDs), so tiles that share a weight slice or an activation block run on
-// the same XCD and share its L2.
+// Workgroup -> logical tile.  Logical tiles are split into 8 contiguous chunks,
+// one per XCD (workgroups are dispatched round-robin over the XCDs), so tiles
+// sharing a weight slice or an activation block run on one XCD and its L2.
 __device__ inline int xcd_tile(int n) {
   const int c = (n + kXcds - 1) / kXcds;
   const int x = blockIdx.x % kXcds, o = blockIdx.x / kXcds;
@@ -53,156 +90,234 @@ __device__ inline int xcd_tile(int n) {
   return i < n ? i : -1;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GateUpArgs gu, DownArgs dn,
-                                                                    CombineArgs cb) {
-  using Tl = Tile<BM, BN, WM, WN>;
-  constexpr int NT = Tl::NT, FM = Tl::FM, FN = Tl::FN, TM = Tl::TM, TN = Tl::TN;
-  constexpr int A_PER = Tl::A_PER, B_PER = Tl::B_PER;
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, DownArgs dn) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::ST, MB = C::MB;
+  constexpr int WN = C::WN, NW = C::NW, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+  constexpr int CPR = C::CPR, RPI = C::RPI, IPW = C::IPW;
 
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN][LDK];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds2[ST > 2 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds3[ST > 3 ? C::STAGE : 8];
+  __shared__ int s_asg[BM];
+  __shared__ float s_wt[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int l16 = lane & 15, lg = lane >> 4;
 
   // ---------------------------------------------------------- tile setup
   int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0;
-  if (MODE == GATE_UP) {
+  if constexpr (MODE == GATE_UP) {
     const int i = xcd_tile(*gu.desc_count);
     if (i < 0) return;
     const TileDesc d = gu.desc[i];
     g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0; K = gu.D;
-  } else if (MODE == DOWN) {
+  } else {
     const int i = xcd_tile(*dn.desc_count);
     if (i < 0) return;
     const TileDesc d = dn.desc[i];
-    g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0; K = dn.F;
-  } else {
-    const int ntiles = cb.D / BN;
-    const int mt = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
-    row0 = mt * BM; rows = min(BM, cb.T - row0); col0 = nt * BN; K = cb.Fs;
+    g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0;
+    K = (g == dn.E) ? dn.Fs : dn.F;
   }
 
-  // per-thread source pointers of the 16-byte chunks it stages each K step
-  const bf16_t* a_src[A_PER];
-  const bf16_t* b_src[B_PER];
+  // DMA sources: instruction q = wave + i*NW covers rows [q*RPI, q*RPI+RPI) of
+  // the stage (A rows first, then B rows); lane l fills physical chunk l % CPR
+  // of row q*RPI + l / CPR, i.e. logical chunk (l % CPR) ^ swz(row).
+  const bf16_t* src[IPW];
 #pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int c = tid + i * NT;
-    const int r = min(c / (BK / 8), rows - 1), ch = c % (BK / 8);
+  for (int i = 0; i < IPW; ++i) {
+    const int q = wave + i * NW;
+    const int r = q * RPI + lane / CPR;
+    const int ch = (lane % CPR) ^ swz<BK>(r);
     const bf16_t* base;
-    if (MODE == GATE_UP) {
-      int tok;
-      if (g == gu.E) tok = row0 + r;
-      else tok = gu.row_assign[gu.offsets[g] + row0 + r] / gu.k;
-      base = gu.x + (size_t)tok * gu.D;
-    } else if (MODE == DOWN) {
-      base = dn.H + (size_t)(dn.offsets[g] + row0 + r) * dn.F;
+    if (r < BM) {
+      const int rr = min(r, rows - 1);  // rows past the tile repeat its last row
+      if constexpr (MODE == GATE_UP) {
+        const int tok = (g == gu.E) ? row0 + rr
+                                    : gu.row_assign[gu.offsets[g] + row0 + rr] / gu.k;
+        base = gu.x + (size_t)tok * gu.D;
+      } else {
+        base = (g == dn.E) ? dn.Hs + (size_t)(row0 + rr) * dn.Fs
+                           : dn.H + (size_t)(dn.offsets[g] + row0 + rr) * dn.F;
+      }
     } else {
-      base = cb.Hs + (size_t)(row0 + r) * cb.Fs;
+      const int n = r - BM;
+      if constexpr (MODE == GATE_UP) {
+        const int blk = n / MB, hcol = col0 + (blk / 2) * MB + (n % MB);
+        const bool up = blk & 1;
+        if (g == gu.E) base = (up ? gu.sw3 : gu.sw1) + (size_t)hcol * gu.D;
+        else base = (up ? gu.w3 : gu.w1) + ((size_t)g * gu.F + hcol) * gu.D;
+      } else {
+        base = (g == dn.E) ? dn.sw2 + (size_t)(col0 + n) * dn.Fs
+                           : dn.w2 + ((size_t)g * dn.D + col0 + n) * dn.F;
+      }
     }
-    a_src[i] = base + ch * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int c = tid + i * NT;
-    const int n = min(c / (BK / 8), BN - 1), ch = c % (BK / 8);
-    const bf16_t* base;
-    if (MODE == GATE_UP) {
-      const int blk = n / 16, hcol = col0 + (blk / 2) * 16 + (n % 16);
-      const bool up = blk & 1;
-      if (g == gu.E) base = (up ? gu.sw3 : gu.sw1) + (size_t)hcol * gu.D;
-      else base = (up ? gu.w3 : gu.w1) + ((size_t)g * gu.F + hcol) * gu.D;
-    } else if (MODE == DOWN) {
-      base = dn.w2 + ((size_t)g * dn.D + col0 + n) * dn.F;
-    } else {
-      base = cb.sw2 + (size_t)(col0 + n) * cb.Fs;
-    }
-    b_src[i] = base + ch * 8;
+    src[i] = base + ch * 8;
   }
 
-  uint4 ra[A_PER], rb[B_PER];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      if (Tl::A_CHUNKS % NT == 0 || tid + i * NT < Tl::A_CHUNKS)
-        ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + kt * BK);
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      if (Tl::B_CHUNKS % NT == 0 || tid + i * NT < Tl::B_CHUNKS)
-        rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + kt * BK);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + i * NT;
-      if (Tl::A_CHUNKS % NT == 0 || c < Tl::A_CHUNKS)
-        *reinterpret_cast<uint4*>(&sA[buf][c / 8][(c % 8) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = tid + i * NT;
-      if (Tl::B_CHUNKS % NT == 0 || c < Tl::B_CHUNKS)
-        *reinterpret_cast<uint4*>(&sB[buf][c / 8][(c % 8) * 8]) = rb[i];
-    }
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int m = 0; m < FM; ++m)
-#pragma unroll
-    for (int n = 0; n < FN; ++n) acc[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  // 16-row blocks of this wave that hold at least one valid row
-  const int live_m = min(FM, max(0, (rows - wm * TM + 15) / 16));
-
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      bf16x8 bfr[FN];
-#pragma unroll
-      for (int n = 0; n < FN; ++n)
-        bfr[n] = *reinterpret_cast<const bf16x8*>(&sB[cur][wn * TN + n * 16 + l16][s * 32 + lg * 8]);
-#pragma unroll
-      for (int m = 0; m < FM; ++m) {
-        if (m < live_m) {
-          const bf16x8 afr =
-              *reinterpret_cast<const bf16x8*>(&sA[cur][wm * TM + m * 16 + l16][s * 32 + lg * 8]);
-#pragma unroll
-          for (int n = 0; n < FN; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[n], acc[m][n], 0, 0, 0);
+  // per-row data of the epilogue, staged once per tile
+  // (row of Y and routing weight of every row of the tile)
+  if constexpr (MODE == DOWN) {
+    for (int r = tid; r < BM; r += C::NT) {
+      if (r < rows) {
+        if (g == dn.E) {
+          s_asg[r] = (row0 + r) * (dn.k + 1) + dn.k;
+          s_wt[r] = 1.0f;
+        } else {
+          const int a = dn.row_assign[dn.offsets[g] + row0 + r];
+          s_asg[r] = y_row(a, dn.k);
+          s_wt[r] = dn.topk_w[a];
         }
       }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  }
+
+  auto stage_ptr = [&](int s) -> bf16_t* {
+    return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3;
+  };
+  auto issue = [&](bf16_t* st, int kt) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int q = wave + i * NW;
+      // (the source goes through void*: a typed pointer here silently drops
+      // the kernel's host-side launch stub)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
+                                       (lds_void*)(st + q * (RPI * BK)), 16, 0, 0);
+    }
+  };
+
+  // rows of this tile handled by each wave row: an even split in MB blocks
+  const int per = min(TM, ((rows + C::WM - 1) / C::WM + MB - 1) / MB * MB);
+  const int wrow0 = wm * per;
+  const int live_m = min(min(FM, per / MB), max(0, (rows - wrow0 + MB - 1) / MB));
+
+  // fragment read offsets (elements, without the stage base and k-chunk)
+  const int lr = lane % MB, lk = lane / MB;
+  const int sw = swz<BK>(lr);
+
+  typedef typename std::conditional<MB == 32, f32x16, f32x4>::type acc_t;
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int m = 0; m < FM; ++m)
+#pragma unroll
+    for (int n = 0; n < FN; ++n) acc[m][n] = acc_t{};
+
+  const int nk = K / BK;
+
+  // Main loop, specialised on the number of live MFMA row blocks (LIVE) so the
+  // inner loop has no branches.  Software pipeline per stage: reads of
+  // sub-step s+1 are issued before the MFMAs of sub-step s, and the stage
+  // hand-over (wait, barrier, refill, next stage's first reads) sits just
+  // before the last sub-step's MFMAs.
+  auto run = [&](auto live_c) {
+    constexpr int LIVE = decltype(live_c)::value;
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto load_frags = [&](const bf16_t* st, int sub, int slot) {
+      const int kc = (MB == 32 ? 2 * sub : 4 * sub) + lk;  // logical 16-byte chunk
+      const int off = (kc ^ sw) * 8;
+      const bf16_t* sa = st + (wrow0 + lr) * BK + off;
+      const bf16_t* sb = st + (BM + wn * TN + lr) * BK + off;
+#pragma unroll
+      for (int n = 0; n < FN; ++n)
+        fb[slot][n] = *reinterpret_cast<const bf16x8*>(sb + n * MB * BK);
+#pragma unroll
+      for (int m = 0; m < LIVE; ++m)
+        fa[slot][m] = *reinterpret_cast<const bf16x8*>(sa + m * MB * BK);
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+      for (int m = 0; m < LIVE; ++m)
+#pragma unroll
+        for (int n = 0; n < FN; ++n) {
+          if constexpr (MB == 32)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][m], fb[slot][n],
+                                                                acc[m][n], 0, 0, 0);
+          else
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][m], fb[slot][n],
+                                                                acc[m][n], 0, 0, 0);
+        }
+    };
+    // prologue: fill every stage, wait for stage 0, read its first fragments
+#pragma unroll
+    for (int s = 0; s < ST; ++s)
+      if (s < nk) issue(stage_ptr(s), s);
+    if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
+    else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+    lds_barrier();
+    load_frags(stage_ptr(0), 0, 0);
+
+    auto step = [&](auto sc, int kt) {
+      constexpr int s = decltype(sc)::value;  // stage of k-step kt
+      bf16_t* cur = stage_ptr(s);
+#pragma unroll
+      for (int sub = 0; sub < C::KSUB; ++sub) {
+        if (sub + 1 < C::KSUB) load_frags(cur, sub + 1, (sub + 1) & 1);
+        if (sub == C::KSUB - 1 && kt + 1 < nk) {
+          // Every read of this stage is issued (the last sub-step's fragments
+          // are in registers), so before its MFMAs: wait for stage kt+1 (stages
+          // kt+2 .. kt+ST-1 may stay in flight), meet the barrier, refill this
+          // stage ST steps ahead and read the next stage's first fragments;
+          // the MFMAs below then cover that read latency.
+          if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 2)));
+          else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+          lds_barrier();
+          if (kt + ST < nk) issue(cur, kt + ST);
+          load_frags(stage_ptr((s + 1) % ST), 0, 0);  // slot 0 is free: sub-step KSUB-2 used it
+        }
+        mma(sub & 1);
+      }
+    };
+    for (int kt = 0; kt < nk; kt += ST) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1 % ST>{}, kt + 1);
+      if constexpr (ST > 2) if (kt + 2 < nk) step(std::integral_constant<int, 2 % ST>{}, kt + 2);
+      if constexpr (ST > 3) if (kt + 3 < nk) step(std::integral_constant<int, 3 % ST>{}, kt + 3);
+    }
+  };
+  static_assert(C::KSUB % 2 == 0, "fragment slots alternate per sub-step");
+  static_assert(FM <= 4, "live-block dispatch covers up to 4 row blocks");
+  switch (live_m) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (FM >= 2) run(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (FM >= 3) run(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (FM >= 4) run(std::integral_constant<int, 4>{}); break;
+    default: {
+      // this wave row holds no valid row: keep the barrier count of the others
+      for (int s = 0; s < ST; ++s)
+        if (s < nk) issue(stage_ptr(s), s);
+      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+      lds_barrier();
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+        lds_barrier();
+        if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST);
+      }
+    }
   }
 
   // ------------------------------------------------------------ epilogue
-  // accumulator element r of block (m, n): row wm*TM + m*16 + 4*lg + r,
-  // column wn*TN + n*16 + l16.
-  if (MODE == GATE_UP) {
+  // accumulator element r of block (m, n):
+  //   MB = 32: row 8*(r/4) + 4*(lane/32) + r%4, column lane % 32
+  //   MB = 16: row 4*(lane/16) + r,             column lane % 16
+  constexpr int NR = MB == 32 ? 16 : 4;
+  auto row_of = [&](int m, int r) {
+    return wrow0 + m * MB + (MB == 32 ? 8 * (r / 4) + 4 * lk + (r % 4) : 4 * lk + r);
+  };
+  if constexpr (MODE == GATE_UP) {
     const bool shared = (g == gu.E);
     const int F = shared ? gu.Fs : gu.F;
-    bf16_t* Hb = shared ? gu.Hs + (size_t)row0 * F
-                        : gu.H + (size_t)(gu.offsets[g] + row0) * F;
+    bf16_t* Hb = shared ? gu.Hs + (size_t)row0 * F : gu.H + (size_t)(gu.offsets[g] + row0) * F;
 #pragma unroll
     for (int m = 0; m < FM; ++m) {
+      if (m >= live_m) continue;
 #pragma unroll
       for (int q = 0; q < FN / 2; ++q) {
-        const int hcol = col0 + (wn * TN / 32 + q) * 16 + l16;
+        const int hcol = col0 + (wn * TN / (2 * MB) + q) * MB + lr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wm * TM + m * 16 + 4 * lg + r;
+        for (int r = 0; r < NR; ++r) {
+          const int row = row_of(m, r);
           if (row < rows) {
             const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
             Hb[(size_t)row * F + hcol] = f32_to_bf16(h);
@@ -210,84 +325,93 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GateUpArgs 
         }
       }
     }
-  } else if (MODE == DOWN) {
-    const int prow0 = dn.offsets[g] + row0;
-#pragma unroll
-    for (int m = 0; m < FM; ++m) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * TM + m * 16 + 4 * lg + r;
-        if (row < rows) {
-          const int a = dn.row_assign[prow0 + row];
-          const float w = dn.topk_w[a];
-          float* y = dn.Y + (size_t)a * dn.D + col0 + wn * TN + l16;
-#pragma unroll
-          for (int n = 0; n < FN; ++n) y[n * 16] = w * acc[m][n][r];
-        }
-      }
-    }
   } else {
 #pragma unroll
     for (int m = 0; m < FM; ++m) {
+      if (m >= live_m) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * TM + m * 16 + 4 * lg + r;
+      for (int r = 0; r < NR; ++r) {
+        const int row = row_of(m, r);
         if (row < rows) {
-          const int t = row0 + row;
-          const int col = col0 + wn * TN + l16;
-          const float* y = cb.Y + (size_t)t * cb.k * cb.D + col;
-          float* o = cb.out + (size_t)t * cb.D + col;
+          const float w = s_wt[row];
+          float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
 #pragma unroll
-          for (int n = 0; n < FN; ++n) {
-            float v = acc[m][n][r];
-            for (int j = 0; j < cb.k; ++j) v += y[(size_t)j * cb.D + n * 16];
-            o[n * 16] = v;
-          }
+          for (int n = 0; n < FN; ++n) y[n * MB] = w * acc[m][n][r];
         }
       }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
-hipError_t launch_one(const GateUpArgs& gu, const DownArgs& dn, const CombineArgs& cb,
-                      unsigned grid, hipStream_t s) {
-  grouped_gemm_kernel<BM, BN, WM, WN, MODE><<<grid, WM * WN * kWave, 0, s>>>(gu, dn, cb);
+// out[t][d] = Y[t][k][d] + Y[t][0][d] + ... + Y[t][k-1][d], four columns per thread.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
+                                                      float* __restrict__ out, int T, int D,
+                                                      int k) {
+  const int D4 = D / 4;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * D4) return;
+  const int t = (int)(i / D4), c = (int)(i % D4);
+  const float4* y = reinterpret_cast<const float4*>(Y + (size_t)t * (k + 1) * D) + c;
+  float4 v = y[(size_t)k * D4];
+  for (int j = 0; j < k; ++j) {
+    const float4 u = y[(size_t)j * D4];
+    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+  }
+  reinterpret_cast<float4*>(out + (size_t)t * D)[c] = v;
+}
+
+// Tile configurations: <BM, BN, BK, WM, WN, stages, MFMA block>.
+using CfgDecode = Cfg<32, 256, 64, 1, 4, 4, 32>;   // few rows per expert: weight streaming
+using CfgMid = Cfg<128, 256, 32, 2, 2, 4, 32>;
+#ifndef GLM_CFG_BIG
+#define GLM_CFG_BIG 256, 256, 64, 2, 4, 2, 32
+#endif
+using CfgBig = Cfg<GLM_CFG_BIG>;  // prefill: 8 waves (two per SIMD), BK 64, 2 stages
+using CfgNarrow = Cfg<32, 64, 64, 1, 2, 4, 16>;    // widths that are not a multiple of 128/256
+
+template <class C, int MODE>
+hipError_t launch_one(const GateUpArgs& gu, const DownArgs& dn, unsigned grid, hipStream_t s) {
+  if (grid == 0) return hipSuccess;
+  grouped_gemm_kernel<C, MODE><<<grid, C::NT, 0, s>>>(gu, dn);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch(GemmShape sh, const GateUpArgs& gu, const DownArgs& dn,
-                    const CombineArgs& cb, unsigned grid, hipStream_t s) {
-  if (sh.BN == 128) {
-    if (sh.BM == 16) return launch_one<16, 128, 1, 4, MODE>(gu, dn, cb, grid, s);
-    if (sh.BM == 64) return launch_one<64, 128, 1, 4, MODE>(gu, dn, cb, grid, s);
-    if (sh.BM == 128) return launch_one<128, 128, 2, 2, MODE>(gu, dn, cb, grid, s);
-  }
-  if constexpr (MODE != GATE_UP) {
-    // output widths that are a multiple of 64 but not of 128
-    if (sh.BN == 64) {
-      if (sh.BM == 16) return launch_one<16, 64, 1, 2, MODE>(gu, dn, cb, grid, s);
-      if (sh.BM == 64) return launch_one<64, 64, 2, 2, MODE>(gu, dn, cb, grid, s);
-      if (sh.BM == 128) return launch_one<128, 64, 2, 2, MODE>(gu, dn, cb, grid, s);
-    }
-  }
+hipError_t dispatch(GemmShape sh, const GateUpArgs& gu, const DownArgs& dn, unsigned grid,
+                    hipStream_t s) {
+  if (sh.BM == CfgDecode::BM && sh.BN == CfgDecode::BN)
+    return launch_one<CfgDecode, MODE>(gu, dn, grid, s);
+  if (sh.BM == CfgMid::BM && sh.BN == CfgMid::BN) return launch_one<CfgMid, MODE>(gu, dn, grid, s);
+  if (sh.BM == CfgBig::BM && sh.BN == CfgBig::BN) return launch_one<CfgBig, MODE>(gu, dn, grid, s);
+  if (sh.BM == CfgNarrow::BM && sh.BN == CfgNarrow::BN)
+    return launch_one<CfgNarrow, MODE>(gu, dn, grid, s);
   return hipErrorInvalidValue;
 }
 
-}  // namespace
+}  // namespace gemm
+
+using namespace gemm;
+
+GemmShape gemm_shape(double rows_per_group, bool wide) {
+  if (!wide) return {CfgNarrow::BM, CfgNarrow::BN};
+  if (rows_per_group <= 24.0) return {CfgDecode::BM, CfgDecode::BN};
+  if (rows_per_group <= 96.0) return {CfgMid::BM, CfgMid::BN};
+  return {CfgBig::BM, CfgBig::BN};
+}
 
 hipError_t launch_gateup_bf16(const GateUpArgs& a, GemmShape sh, hipStream_t s) {
-  return dispatch<GATE_UP>(sh, a, DownArgs{}, CombineArgs{}, (unsigned)a.grid, s);
+  return dispatch<GATE_UP>(sh, a, DownArgs{}, (unsigned)a.grid, s);
 }
 
 hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s) {
-  return dispatch<DOWN>(sh, GateUpArgs{}, a, CombineArgs{}, (unsigned)a.grid, s);
+  return dispatch<DOWN>(sh, GateUpArgs{}, a, (unsigned)a.grid, s);
 }
 
-hipError_t launch_shared_combine_bf16(const CombineArgs& a, GemmShape sh, hipStream_t s) {
-  const unsigned grid = (unsigned)(cdiv(a.T, sh.BM) * (a.D / sh.BN));
-  return dispatch<SHARED_COMBINE>(sh, GateUpArgs{}, DownArgs{}, a, grid, s);
+hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, hipStream_t s) {
+  const size_t n = (size_t)T * (D / 4);
+  if (n == 0) return hipSuccess;
+  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(Y, out, T, D, k);
+  return hipGetLastError();
 }
 
 }  // namespace glm

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void down_f32_kernel(F32Args a) {
   const int e = expert_of_row(a.offsets, a.E, r);
   const float y = dot(a.H + (size_t)r * a.F, a.w2 + ((size_t)e * a.D + d) * a.F, a.F);
   const int asg = a.row_assign[r];
-  a.Y[(size_t)asg * a.D + d] = a.topk_w[asg] * y;
+  a.Y[(size_t)y_row(asg, a.k) * a.D + d] = a.topk_w[asg] * y;
 }
 
 __global__ __launch_bounds__(256) void shared_combine_f32_kernel(F32Args a) {
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void shared_combine_f32_kernel(F32Args a) {
   if (i >= (size_t)a.T * a.D) return;
   const int t = (int)(i / a.D), d = (int)(i % a.D);
   float v = dot(a.Hs + (size_t)t * a.Fs, a.sw2 + (size_t)d * a.Fs, a.Fs);
-  for (int j = 0; j < a.k; ++j) v += a.Y[((size_t)t * a.k + j) * a.D + d];
+  for (int j = 0; j < a.k; ++j) v += a.Y[((size_t)t * (a.k + 1) + j) * a.D + d];
   a.out[i] = v;
 }
 

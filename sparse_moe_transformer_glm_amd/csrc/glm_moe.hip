@@ -31,18 +31,12 @@ struct Plan {
   bool bf16;
   int ntiles;        // 64-token routing tiles
   int ksplit, kchunk;
-  GemmShape gu, dn, sc;
+  GemmShape gu, dn;
   int gu_cap, dn_cap;
   size_t partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
       dn_desc, row_assign, H, Hs, Y;
   size_t total;
 };
-
-GemmShape pick_shape(double rows_per_group) {
-  if (rows_per_group <= 16.0) return {16, 128};
-  if (rows_per_group <= 64.0) return {64, 128};
-  return {128, 128};
-}
 
 int desc_cap(int A, int E, GemmShape s, int ncol_tiles) {
   const long nz = A < E ? A : E;
@@ -88,16 +82,14 @@ int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
     P.kchunk = cdiv(ksteps, ks) * 64;
     P.ksplit = cdiv(P.D, P.kchunk);
     const double per_expert = (double)A / P.E;
-    P.gu = pick_shape(per_expert);
-    P.dn = pick_shape(per_expert);
-    P.sc = pick_shape((double)T);
-    // down and shared-combine tile the hidden width D (a multiple of 64)
-    if (P.D % 128) P.dn.BN = P.sc.BN = 64;
+    P.gu = gemm_shape(per_expert, P.F % 128 == 0 && P.Fs % 128 == 0);
+    P.dn = gemm_shape(per_expert, P.D % 256 == 0);
+    // routed tiles, then the shared expert's tiles (group E)
     P.gu_cap = desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN) + cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
-    P.dn_cap = desc_cap(A, P.E, P.dn, P.D / P.dn.BN);
+    P.dn_cap = desc_cap(A, P.E, P.dn, P.D / P.dn.BN) + cdiv(T, P.dn.BM) * (P.D / P.dn.BN);
   } else {
     P.ksplit = 1; P.kchunk = P.D;
-    P.gu = P.dn = P.sc = GemmShape{0, 0};
+    P.gu = P.dn = GemmShape{0, 0};
     P.gu_cap = P.dn_cap = 0;
   }
 
@@ -118,7 +110,7 @@ int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
   P.row_assign = take((size_t)A * 4);
   P.H = take((size_t)A * P.F * act);
   P.Hs = take((size_t)T * P.Fs * act);
-  P.Y = take((size_t)A * P.D * 4);
+  P.Y = take((size_t)T * (top_k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
   P.total = T == 0 ? 0 : o;
   return GLM_MOE_OK;
 }
@@ -180,10 +172,10 @@ int run_router(const Plan& P, const void* x, const float* router_w, const float*
   GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
   if (P.bf16)
     GLM_HIP(launch_router_logits_bf16(static_cast<const bf16_t*>(x), router_w, partial, P.T, P.D,
-                                      P.E, P.ksplit, P.kchunk, s));
+                                      P.E, P.ksplit, P.kchunk, masks, s));
   else
     GLM_HIP(launch_router_logits_f32(static_cast<const float*>(x), router_w, partial, P.T, P.D,
-                                     P.E, s));
+                                     P.E, masks, s));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
   GLM_HIP(launch_router_topk(partial, P.ksplit, corr_bias, P.T, P.E, P.k, scale, idx, w, masks, s));
   return GLM_MOE_OK;
@@ -290,19 +282,16 @@ int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* ro
     GLM_HIP(launch_gateup_bf16(ga, P.gu, s));
 
     DownArgs da{};
-    da.H = ga.H; da.row_assign = row_assign; da.offsets = offsets;
-    da.w2 = static_cast<const bf16_t*>(w2); da.topk_w = wts;
-    da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
-    da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.k = P.k;
+    da.H = ga.H; da.Hs = ga.Hs; da.row_assign = row_assign; da.offsets = offsets;
+    da.w2 = static_cast<const bf16_t*>(w2); da.sw2 = static_cast<const bf16_t*>(shared_w2);
+    da.topk_w = wts; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
+    da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
     da.grid = cdiv(P.dn_cap, kXcds) * kXcds;
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
     GLM_HIP(launch_down_bf16(da, P.dn, s));
 
-    CombineArgs ca{};
-    ca.Hs = ga.Hs; ca.sw2 = static_cast<const bf16_t*>(shared_w2); ca.Y = Y; ca.out = out;
-    ca.T = P.T; ca.D = P.D; ca.Fs = P.Fs; ca.k = P.k;
     GLM_HIP(rec.mark(GLM_MOE_STAGE_SHARED_COMBINE));
-    GLM_HIP(launch_shared_combine_bf16(ca, P.sc, s));
+    GLM_HIP(launch_combine(Y, out, P.T, P.D, P.k, s));
   } else {
     F32Args fa{};
     fa.x = static_cast<const float*>(x);

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __shared__ int s_cnt[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_gu[kMaxExperts + 2];
-  __shared__ int s_dn[kMaxExperts + 1];
+  __shared__ int s_dn[kMaxExperts + 2];
 
   const int tid = threadIdx.x;
   const int e = tid % kMaxExperts, q = tid / kMaxExperts;
@@ -59,10 +59,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
       dn += cdiv(c, p.dn.BM) * dn_nt;
     }
     s_off[E] = off;
+    // the shared expert is group E of both GEMMs, over every token
     s_gu[E] = gu;
-    gu += cdiv(p.T, p.gu.BM) * gu_nts;  // the shared expert: every token
+    gu += cdiv(p.T, p.gu.BM) * gu_nts;
     s_gu[E + 1] = min(gu, p.gu_desc_cap);
-    s_dn[E] = min(dn, p.dn_desc_cap);
+    s_dn[E] = dn;
+    dn += cdiv(p.T, p.dn.BM) * dn_nt;
+    s_dn[E + 1] = min(dn, p.dn_desc_cap);
   }
   __syncthreads();
 
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   if (tid <= E) offsets[tid] = s_off[tid];
   if (tid == 0) {
     *gu_count = s_gu[E + 1];
-    *dn_count = s_dn[E];
+    *dn_count = s_dn[E + 1];
   }
 
   // row base of every (token tile, expert)
@@ -103,21 +106,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     d.col0 = nt * (p.gu.BN / 2);
     gu_desc[i] = d;
   }
-  const int dn_total = s_dn[E];
+  const int dn_total = s_dn[E + 1];
   for (int i = tid; i < dn_total; i += kScanThreads) {
-    int lo = 0, hi = E - 1;
+    int lo = 0, hi = E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_dn[mid] <= i) lo = mid; else hi = mid - 1;
     }
     const int g = lo;
-    const int mt = cdiv(s_cnt[g], p.dn.BM);
+    const int grows = g < E ? s_cnt[g] : p.T;
+    const int mt = cdiv(grows, p.dn.BM);
     const int local = i - s_dn[g];
     const int nt = local / mt, m = local % mt;
     TileDesc d;
     d.group = g;
     d.row0 = m * p.dn.BM;
-    d.rows = min(p.dn.BM, s_cnt[g] - d.row0);
+    d.rows = min(p.dn.BM, grows - d.row0);
     d.col0 = nt * p.dn.BN;
     dn_desc[i] = d;
   }

@@ -41,7 +41,13 @@ __device__ inline void split3(const float4 w0, const float4 w1, bf16x8& hi, bf16
 // operands; the accumulator holds rows 4*(l/16)+r, column l % 16.
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
-    int T, int D, int E, int kchunk) {
+    int T, int D, int E, int kchunk, uint64_t* __restrict__ masks, int n_masks) {
+  // clear the routing masks the top-k kernel fills (the grid has enough threads)
+  {
+    const int b = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int i = b * 256 + threadIdx.x;
+    if (i < n_masks) masks[i] = 0ull;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
   const int t0 = blockIdx.x * 64;
@@ -91,8 +97,9 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 // fp32 activations: plain fp32 dot products, one thread per (token, expert).
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
-    int T, int D, int E) {
+    int T, int D, int E, uint64_t* __restrict__ masks, int n_masks) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (size_t)n_masks) masks[i] = 0ull;  // T*E threads >= masks
   if (i >= (size_t)T * E) return;
   const int t = (int)(i / E), e = (int)(i % E);
   const float* xr = x + (size_t)t * D;
@@ -109,104 +116,110 @@ __device__ inline uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One workgroup per 64-token tile, four waves, one wave per token at a time.
-// Lane l holds experts l, l+64, l+128, l+192.  Selection takes k rounds of a
-// wave-wide max over 64-bit keys (biased score, then lower index).
+// Sum of the K-slice partial logits in slice order (independent loads first).
+__device__ inline float sum_partials(const float* p, size_t stride, int ksplit) {
+  float z = 0.f;
+  int s = 0;
+  for (; s + 8 <= ksplit; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(size_t)(s + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z += v[i];
+  }
+  for (; s < ksplit; ++s) z += p[(size_t)s * stride];
+  return z;
+}
+
+// One wave per token (four tokens per workgroup).  Lane l holds experts l,
+// l+64, l+128, l+192.  Selection takes k rounds of a wave-wide max over 64-bit
+// keys (biased score, then lower index).  Each selection also sets the token's
+// bit in masks[token / 64][expert] (an OR, so the result does not depend on
+// the order of the atomics); the logits kernel has zeroed the masks.
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ partial, int ksplit, const float* __restrict__ bias,
     int T, int E, int k, float scale, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out, uint64_t* __restrict__ masks) {
-  __shared__ unsigned long long smask[kMaxExperts];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  smask[threadIdx.x] = 0ull;
-  __syncthreads();
-
-  const int tile = blockIdx.x;
-  float b[4];
+    float* __restrict__ w_out, unsigned long long* __restrict__ masks) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t stride = (size_t)T * E;
+  float sig[4];
+  unsigned long long key[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
-    b[c] = e < E ? bias[e] : 0.f;
-  }
-
-  for (int i = 0; i < 16; ++i) {
-    const int tl = wave * 16 + i;
-    const int t = tile * kTokTile + tl;
-    if (t >= T) break;
-    float sig[4];
-    unsigned long long key[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      sig[c] = 0.f;
-      key[c] = 0ull;
-      if (e < E) {
-        float z = 0.f;
-        for (int s = 0; s < ksplit; ++s) z += partial[((size_t)s * T + t) * E + e];
-        const float sg = 1.0f / (1.0f + expf(-z));
-        sig[c] = sg;
-        key[c] = ((unsigned long long)ordered_bits(sg + b[c]) << 32) | (uint32_t)(~e);
-      }
-    }
-    float ssum = 0.f, my_sig = 0.f;
-    int my_e = -1;
-    for (int j = 0; j < k; ++j) {
-      unsigned long long best = key[0];
-#pragma unroll
-      for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(best, off, 64);
-        best = o > best ? o : best;
-      }
-      const int es = (int)(~(uint32_t)best);
-      const int src = es & 63, cs = es >> 6;
-      float mine = sig[0];
-#pragma unroll
-      for (int c = 1; c < 4; ++c) mine = (cs == c) ? sig[c] : mine;
-      const float ss = __shfl(mine, src, 64);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (lane == src && cs == c) key[c] = 0ull;
-      ssum += ss;
-      if (lane == j) {
-        my_e = es;
-        my_sig = ss;
-      }
-      if (lane == 0) atomicOr(&smask[es], 1ull << tl);
-    }
-    if (lane < k) {
-      idx_out[(size_t)t * k + lane] = my_e;
-      w_out[(size_t)t * k + lane] = (my_sig / ssum) * scale;
+    sig[c] = 0.f;
+    key[c] = 0ull;
+    if (e < E) {
+      const float z = sum_partials(partial + (size_t)t * E + e, stride, ksplit);
+      const float sg = 1.0f / (1.0f + expf(-z));
+      sig[c] = sg;
+      key[c] = ((unsigned long long)ordered_bits(sg + bias[e]) << 32) | (uint32_t)(~e);
     }
   }
-  __syncthreads();
-  if ((int)threadIdx.x < E) masks[(size_t)tile * E + threadIdx.x] = smask[threadIdx.x];
+  unsigned long long* tmask = masks + (size_t)(t / kTokTile) * E;
+  const unsigned long long bit = 1ull << (t % kTokTile);
+  float ssum = 0.f, my_sig = 0.f;
+  int my_e = -1;
+  for (int j = 0; j < k; ++j) {
+    unsigned long long best = key[0];
+#pragma unroll
+    for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned long long o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
+    }
+    const int es = (int)(~(uint32_t)best);
+    const int src = es & 63, cs = es >> 6;
+    float mine = sig[0];
+#pragma unroll
+    for (int c = 1; c < 4; ++c) mine = (cs == c) ? sig[c] : mine;
+    const float ss = __shfl(mine, src, 64);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (lane == src && cs == c) key[c] = 0ull;
+    ssum += ss;
+    if (lane == j) {
+      my_e = es;
+      my_sig = ss;
+    }
+  }
+  if (lane < k) {
+    idx_out[(size_t)t * k + lane] = my_e;
+    w_out[(size_t)t * k + lane] = (my_sig / ssum) * scale;
+    atomicOr(&tmask[my_e], bit);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_router_logits_bf16(const bf16_t* x, const float* router_w, float* partial,
                                      int T, int D, int E, int ksplit, int kchunk,
-                                     hipStream_t s) {
+                                     uint64_t* masks, hipStream_t s) {
   dim3 grid(cdiv(T, 64), cdiv(E, 64), ksplit);
-  router_logits_bf16_kernel<<<grid, 256, 0, s>>>(x, router_w, partial, T, D, E, kchunk);
+  // masks: ceil(T/64) * E <= ceil(T/64) * 256 <= number of threads
+  const int n_masks = cdiv(T, kTokTile) * E;
+  router_logits_bf16_kernel<<<grid, 256, 0, s>>>(x, router_w, partial, T, D, E, kchunk, masks,
+                                                 n_masks);
   return hipGetLastError();
 }
 
 hipError_t launch_router_logits_f32(const float* x, const float* router_w, float* partial,
-                                    int T, int D, int E, hipStream_t s) {
+                                    int T, int D, int E, uint64_t* masks, hipStream_t s) {
   const size_t n = (size_t)T * E;
-  router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, router_w, partial,
-                                                                         T, D, E);
+  router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+      x, router_w, partial, T, D, E, masks, cdiv(T, kTokTile) * E);
   return hipGetLastError();
 }
 
 hipError_t launch_router_topk(const float* partial, int ksplit, const float* corr_bias, int T,
                               int E, int k, float scale, int32_t* topk_idx, float* topk_w,
                               uint64_t* masks, hipStream_t s) {
-  router_topk_kernel<<<cdiv(T, kTokTile), 256, 0, s>>>(partial, ksplit, corr_bias, T, E, k,
-                                                        scale, topk_idx, topk_w, masks);
+  router_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(partial, ksplit, corr_bias, T, E, k, scale,
+                                               topk_idx, topk_w,
+                                               reinterpret_cast<unsigned long long*>(masks));
   return hipGetLastError();
 }
 

@@ -47,6 +47,13 @@ def test_exports_are_c_linkage_only():
         "internal symbols are exported"
 
 
+def test_no_undefined_internal_symbols():
+    out = subprocess.run(["nm", "-D", "--undefined-only", glm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [l for l in out.splitlines() if "glm" in l]
+    assert not bad, bad
+
+
 def _ws(T, D, E, F, Fs, k, dt=glm.BF16):
     n = ctypes.c_size_t(0)
     st = glm.lib().glm_moe_workspace_size(ctypes.byref(Dims(T, D, E, F, Fs, dt, dt)), k,
