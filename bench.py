@@ -36,22 +36,24 @@ def algorithmic(w, counts):
     n_active = int((counts > 0).sum())
     wb = 2  # bf16 weight bytes
     f = {
+        # routed and shared gate/up (one launch)
         "gate_up": 2.0 * T * k * 2 * F * D + 2.0 * T * 2 * Fs * D,
-        "down": 2.0 * T * k * D * F,
-        "shared_combine": 2.0 * T * D * Fs,
+        # routed and shared down projections (one launch)
+        "down": 2.0 * T * k * D * F + 2.0 * T * D * Fs,
+        "shared_combine": 0.0,
         "router_fp32": 2.0 * T * E * D,
     }
     b = {
         # active experts' w1+w3, the shared w1+w3, and the input tokens
         "gate_up": (n_active * 2 * F * D + 2 * Fs * D) * wb + T * D * 2,
-        # active experts' w2
-        "down": n_active * D * F * wb,
-        # shared w2 and the fp32 output
-        "shared_combine": D * Fs * wb + T * D * 4,
+        # active experts' w2 and the shared w2
+        "down": (n_active * D * F + D * Fs) * wb,
+        # the combine writes the fp32 output (its slot-buffer reads are overhead)
+        "shared_combine": T * D * 4,
     }
     layer_bytes = ((n_active * 3 * F * D + 3 * Fs * D) * wb + E * D * 4 + E * 4
                    + T * D * 2 + T * D * 4)
-    layer_flops = f["gate_up"] + f["down"] + f["shared_combine"]
+    layer_flops = f["gate_up"] + f["down"]
     return f, b, layer_flops, layer_bytes, n_active
 
 
