@@ -24,6 +24,30 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s @GLM-5.2 shape (T=64 decode, T=8192 prefill); % roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gate_up_glm.json")
+KERNEL_SOURCES = ("gemm_bf16.hip", "common.h")
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_transformer_glm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC) as fh:
+            d = json.load(fh)
+    except OSError:
+        return None
+    if d.get("kernel_source_sha256") != kernel_source_sha() or kind not in d:
+        return None
+    return d[kind]["hbm_bytes_per_launch"]
 
 
 def log(msg):
@@ -79,7 +103,7 @@ def time_layer(glm, torch, dev, w, steps, warmup, ws):
     return elapsed, per_call, counts
 
 
-def record(w, elapsed, steps, per_call, counts, bound):
+def record(w, elapsed, steps, per_call, counts, bound, traffic_kind=None):
     f, b, lf, lb, n_active = algorithmic(w, counts)
     ms = elapsed * 1e3 / steps
     dom = max(("gate_up", "down", "shared_combine"), key=lambda s: per_call[s])
@@ -89,11 +113,15 @@ def record(w, elapsed, steps, per_call, counts, bound):
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": None, "work_per_launch": f[dom], "avg_launch_ms": round(per_call[dom], 4)}
+        if dom == "gate_up" and traffic_kind:
+            roof["traffic"] = measured_traffic(traffic_kind)
     else:
         ach = b[dom] / t_dom / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
                 "work_per_launch": b[dom], "avg_launch_ms": round(per_call[dom], 4)}
+        if dom == "gate_up" and traffic_kind:
+            roof["traffic"] = measured_traffic(traffic_kind)
     t_layer = ms * 1e-3
     layer = {"tflops": round(lf / t_layer / 1e12, 2),
              "frac_mfma": round(lf / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -145,7 +173,9 @@ def main():
     ap.add_argument("--workload", default="glm_prefill")
     ap.add_argument("--decode-workload", default="glm_decode", help="'' to skip")
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="0 to skip the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=48, help="0 to skip the oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -176,7 +206,8 @@ def main():
     ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
 
     elapsed, per_call, counts = time_layer(glm, torch, dev, wp, args.steps, args.warmup, ws)
-    ms, roof, layer, load = record(wp, elapsed, args.steps, per_call, counts, "mfma")
+    ms, roof, layer, load = record(wp, elapsed, args.steps, per_call, counts, "mfma",
+                                   "prefill" if wp.name == "glm_prefill" else None)
     value = wp.T * args.steps / elapsed
     log(f"prefill: {value:,.0f} tokens/s, {ms:.3f} ms/step, stages {per_call}")
 
@@ -198,7 +229,8 @@ def main():
                        to_device(wl.make_corr_bias(wd)), dev.w1, dev.w3, dev.w2, dev.sw1,
                        dev.sw3, dev.sw2)
         e2, pc2, c2 = time_layer(glm, torch, dd, wd, args.decode_steps, args.warmup, ws)
-        ms2, roof2, layer2, load2 = record(wd, e2, args.decode_steps, pc2, c2, "hbm")
+        ms2, roof2, layer2, load2 = record(wd, e2, args.decode_steps, pc2, c2, "hbm",
+                                           "decode" if wd.name == "glm_decode" else None)
         v2 = wd.T * args.decode_steps / e2
         log(f"decode: {v2:,.0f} tokens/s, {ms2:.3f} ms/step, stages {pc2}")
         line["decode"] = {"workload": wd.name, "tokens": wd.T, "value": round(v2, 1),
@@ -209,6 +241,13 @@ def main():
 
     del dev
     torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     if args.cpu_tokens > 0:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
         line["cpu_baseline"] = cpu_baseline(wp, args.cpu_tokens)
