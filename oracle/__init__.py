@@ -3,8 +3,10 @@
 TEST INFRASTRUCTURE ONLY: importable by ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py``; never by the product package.
 """
-from .moe import (Routing, bf16_bits_to_f64, decode, expert_load, expert_mlp, forward,
-                  forward_arrays, route, select_topk, sigmoid, silu, topk_gap)
+from .moe import (Routing, bf16_bits_to_f64, block_ffn, decode, dense_ffn, expert_load,
+                  expert_mlp, forward, forward_arrays, group_scores, rmsnorm, round_bf16, route,
+                  select_topk, select_topk_grouped, sigmoid, silu, topk_gap)
 
-__all__ = ["Routing", "bf16_bits_to_f64", "decode", "expert_load", "expert_mlp", "forward",
-           "forward_arrays", "route", "select_topk", "sigmoid", "silu", "topk_gap"]
+__all__ = ["Routing", "bf16_bits_to_f64", "block_ffn", "decode", "dense_ffn", "expert_load",
+           "expert_mlp", "forward", "forward_arrays", "group_scores", "rmsnorm", "round_bf16",
+           "route", "select_topk", "select_topk_grouped", "sigmoid", "silu", "topk_gap"]

@@ -68,6 +68,38 @@ def select_topk(beta: np.ndarray, k: int) -> np.ndarray:
     return order[..., :k]
 
 
+def select_topk_grouped(beta: np.ndarray, k: int, n_group: int, topk_group: int,
+                        group_topk: int = 2) -> np.ndarray:
+    """Group-limited top-k.
+
+    Experts form ``n_group`` consecutive groups.  A group's score is the sum of
+    its ``group_topk`` largest biased scores; each token keeps the
+    ``topk_group`` best groups (equal scores: lower group index), and the k
+    experts are then the top-k of the biased scores inside the kept groups
+    (same order and tie rule as ``select_topk``).  ``n_group == 1`` is plain
+    top-k.
+    """
+    T, E = beta.shape
+    if n_group <= 1:
+        return select_topk(beta, k)
+    gs = E // n_group
+    grouped = beta.reshape(T, n_group, gs)
+    top_in_group = -np.sort(-grouped, axis=2)[:, :, :group_topk]
+    gscore = top_in_group.sum(axis=2)
+    keep = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, keep, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), beta, -np.inf)
+    return select_topk(masked, k)
+
+
+def group_scores(beta: np.ndarray, n_group: int, group_topk: int = 2) -> np.ndarray:
+    """Per-token group scores used by ``select_topk_grouped`` ([T, n_group])."""
+    T, E = beta.shape
+    g = beta.reshape(T, n_group, E // n_group)
+    return (-np.sort(-g, axis=2)[:, :, :group_topk]).sum(axis=2)
+
+
 @dataclasses.dataclass
 class Routing:
     idx: np.ndarray      # [T, k] int64, slot order
@@ -77,12 +109,14 @@ class Routing:
 
 
 def route(x, router_w, corr_bias, top_k: int, scale: float,
-          force_idx: Optional[np.ndarray] = None) -> Routing:
+          force_idx: Optional[np.ndarray] = None, n_group: int = 1, topk_group: int = 1,
+          group_topk: int = 2) -> Routing:
     """Steps 1-4 of the layer.
 
     1. z = x W_r^T, sigma = 1 / (1 + exp(-z))           (sigmoid router scores)
     2. beta = sigma + b                                   (correction bias)
-    3. idx = top_k of beta, ties to the lower index       (selection)
+    3. idx = top_k of beta, ties to the lower index       (selection; with
+       n_group > 1, only inside the token's topk_group best expert groups)
     4. w_j = (sigma[idx_j] / sum_i sigma[idx_i]) * scale  (un-biased renormalise, then x2.5)
 
     ``force_idx`` replaces step 3 (used to evaluate the layer on a selection
@@ -95,7 +129,7 @@ def route(x, router_w, corr_bias, top_k: int, scale: float,
     sigma = sigmoid(z)
     beta = sigma + b[None, :]
     if force_idx is None:
-        idx = select_topk(beta, top_k)
+        idx = select_topk_grouped(beta, top_k, n_group, topk_group, group_topk)
     else:
         idx = np.asarray(force_idx, dtype=np.int64)
     sel = np.take_along_axis(sigma, idx, axis=1)
@@ -130,7 +164,9 @@ def forward(x, router_w, corr_bias,
             shared: Expert,
             top_k: int, scale: float,
             force_idx: Optional[np.ndarray] = None,
-            routing: Optional[Routing] = None) -> Tuple[np.ndarray, Routing]:
+            routing: Optional[Routing] = None,
+            n_group: int = 1, topk_group: int = 1,
+            group_topk: int = 2) -> Tuple[np.ndarray, Routing]:
     """The whole layer: returns ``(out [T, D] float64, routing)``.
 
     ``experts(e)`` returns routed expert e's ``(w1, w3, w2)`` (any dtype that
@@ -142,7 +178,8 @@ def forward(x, router_w, corr_bias,
     6. out = routed + MLP_shared(x)                      (always-on shared expert)
     """
     xd = decode(x)
-    r = routing if routing is not None else route(xd, router_w, corr_bias, top_k, scale, force_idx)
+    r = routing if routing is not None else route(xd, router_w, corr_bias, top_k, scale, force_idx,
+                                                  n_group, topk_group, group_topk)
     T, D = xd.shape
     routed = np.zeros((T, D))
     for e in np.unique(r.idx):
@@ -164,3 +201,39 @@ def forward_arrays(x, router_w, corr_bias, w1, w3, w2, sw1, sw3, sw2,
 def expert_load(idx: np.ndarray, E: int) -> np.ndarray:
     """Number of (token, slot) assignments per expert (the utilisation histogram)."""
     return np.bincount(np.asarray(idx).reshape(-1), minlength=E)
+
+
+# ------------------------------------------------ block around the layer
+
+def rmsnorm(h: np.ndarray, weight, eps: float) -> np.ndarray:
+    """h / sqrt(mean(h^2) + eps) * weight, per row."""
+    h = decode(h)
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps) * decode(weight)
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of float64 values (finite inputs)."""
+    f = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(f)                     # f = m * 2^e, 0.5 <= |m| < 1
+    q = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)  # keep 8 significant bits, ties to even
+    return q
+
+
+def block_ffn(h, norm_weight, eps: float, x_dtype: str, layer) -> Tuple[np.ndarray, object]:
+    """The pre-norm block's feed-forward half: h + FFN(RMSNorm(h)).
+
+    ``layer(x)`` is the feed-forward (the MoE layer or a dense MLP) and returns
+    (out, extra).  The normalised input is held in the activation dtype
+    (``x_dtype`` "bf16" rounds it to bf16, "f32" to fp32), as the layer
+    receives it in a model of that dtype.
+    """
+    hd = decode(h)
+    xn = rmsnorm(hd, norm_weight, eps)
+    xn = round_bf16(xn) if x_dtype == "bf16" else xn.astype(np.float32).astype(np.float64)
+    out, extra = layer(xn)
+    return hd + out, extra
+
+
+def dense_ffn(x, w1, w3, w2) -> np.ndarray:
+    """A dense SiLU-gated MLP (the leading dense layers use this form)."""
+    return expert_mlp(decode(x), w1, w3, w2)
