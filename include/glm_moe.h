@@ -154,6 +154,64 @@ GLM_MOE_API int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, con
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            glm_moe_trace* trace);
 
+/* Options around the layer (all optional; a null options pointer, or a
+ * zeroed struct, gives the plain GLM-5.2 layer above).
+ *   n_group, topk_group, group_topk: group-limited routing as GLM-4.5 uses
+ *     it ("Full Forward" GLM-4.5 note, How it works: sigmoid group routing).
+ *     The E experts form n_group consecutive groups (E % n_group == 0); a
+ *     group's score is the sum of its group_topk largest biased scores; each
+ *     token keeps its topk_group best groups (equal scores: lower group) and
+ *     picks its top_k experts inside them.  n_group 0 or 1 disables grouping;
+ *     group_topk 0 means min(2, E / n_group).  Requires topk_group * E / n_group >= top_k and
+ *     n_group <= 64.
+ *   norm_weight, norm_eps: when norm_weight ([D] fp32) is given, x is the
+ *     pre-norm residual stream h of the block and the layer runs on
+ *     RMSNorm(h) = h / sqrt(mean(h^2) + eps) * norm_weight, computed in fp32
+ *     and held in act_dtype (the pre-norm block of the "Full Forward" note).
+ *   add_residual: nonzero adds x (the residual stream) to the output:
+ *     out = x + layer(...), the block's residual add, done in fp32 after the
+ *     shared and routed terms. */
+typedef struct {
+  int32_t n_group;
+  int32_t topk_group;
+  int32_t group_topk;
+  const float* norm_weight;
+  float norm_eps;
+  int32_t add_residual;
+} glm_moe_options;
+
+/* glm_moe_workspace_size / glm_moe_route / glm_moe_forward_traced with
+ * options (`opts` nullable).  Same conventions and error codes; invalid
+ * options return GLM_MOE_EINVAL (or EUNSUPPORTED for n_group > 64). */
+GLM_MOE_API int glm_moe_workspace_size_ex(const glm_moe_dims* d, const glm_moe_options* opts,
+                                          int top_k, size_t* bytes);
+GLM_MOE_API int glm_moe_route_ex(const glm_moe_dims* d, const glm_moe_options* opts,
+                                 const void* x, const float* router_w, const float* corr_bias,
+                                 int top_k, float scale, int32_t* topk_idx, float* topk_w,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+GLM_MOE_API int glm_moe_forward_ex(const glm_moe_dims* d, const glm_moe_options* opts,
+                                   const void* x, const float* router_w, const float* corr_bias,
+                                   const void* w1, const void* w3, const void* w2,
+                                   const void* shared_w1, const void* shared_w3,
+                                   const void* shared_w2, int top_k, float scale, float* out,
+                                   int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream,
+                                   glm_moe_trace* trace);
+
+/* A dense SiLU-gated feed-forward layer, out = w2 (SiLU(w1 x) * (w3 x)): the
+ * leading dense layers of the model (GLM-5.2 anatomy page, Token path: 3
+ * dense FFN blocks before the MoE blocks), run on the same grouped kernels as
+ * one group.  Uses d->T, d->D, d->F_shared (the dense width) and the dtypes;
+ * E and F are ignored.  w1, w3 [F_shared][D]; w2 [D][F_shared]; out [T][D]
+ * fp32.  opts may give norm_weight / norm_eps / add_residual (grouping
+ * fields are ignored).  Workspace from glm_moe_dense_workspace_size. */
+GLM_MOE_API int glm_moe_dense_workspace_size(const glm_moe_dims* d, const glm_moe_options* opts,
+                                             size_t* bytes);
+GLM_MOE_API int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* opts,
+                                  const void* x, const void* w1, const void* w3, const void* w2,
+                                  float* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Static text for a status code. */
 GLM_MOE_API const char* glm_moe_status_string(int status);
 

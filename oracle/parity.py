@@ -38,31 +38,68 @@ class RoutingReport:
         return not self.invalid
 
 
+def _near_topk(b: np.ndarray, sel: np.ndarray, k: int, tie_eps: float) -> bool:
+    """``sel`` (slot order) is a top-k of the scores ``b`` up to ``tie_eps``."""
+    chosen = b[sel]
+    kth = -np.sort(-b)[k - 1]
+    rest = np.delete(b, sel)
+    return bool(chosen.min() >= kth - tie_eps
+                and (rest.size == 0 or rest.max() <= chosen.min() + tie_eps)
+                and (np.diff(chosen) <= tie_eps).all())
+
+
+def _valid_choice(b: np.ndarray, sel: np.ndarray, k: int, n_group: int, topk_group: int,
+                  group_topk: int, tie_eps: float) -> bool:
+    E = b.size
+    if len(set(sel.tolist())) != k or sel.min() < 0 or sel.max() >= E:
+        return False
+    if n_group <= 1:
+        return _near_topk(b, sel, k, tie_eps)
+    # Group-limited: the kept groups must hold every chosen expert and be a
+    # top-topk_group set of group scores (each a sum of group_topk scores, so
+    # its tolerance is group_topk * tie_eps); the experts must then be a
+    # top-k inside the kept groups.  Groups not implied by the choice are
+    # filled with the best remaining ones.
+    gs = E // n_group
+    gscore = moe.group_scores(b[None, :], n_group, group_topk)[0]
+    used = sorted(set((sel // gs).tolist()))
+    if len(used) > topk_group:
+        return False
+    others = [g for g in np.argsort(-gscore, kind="stable") if g not in used]
+    kept = np.array(used + others[:topk_group - len(used)], dtype=np.int64)
+    geps = group_topk * tie_eps
+    kth_g = -np.sort(-gscore)[topk_group - 1]
+    dropped = np.delete(gscore, kept)
+    if gscore[kept].min() < kth_g - geps:
+        return False
+    if dropped.size and dropped.max() > gscore[kept].min() + geps:
+        return False
+    allowed = np.concatenate([np.arange(g * gs, (g + 1) * gs) for g in sorted(kept)])
+    pos = {int(e): i for i, e in enumerate(allowed)}
+    return _near_topk(b[allowed], np.array([pos[int(e)] for e in sel]), k, tie_eps)
+
+
 def compare_routing(idx: np.ndarray, w: np.ndarray, x, router_w, corr_bias, k: int,
                     scale: float, ref: Optional[moe.Routing] = None,
-                    tie_eps: float = 1e-5) -> RoutingReport:
+                    tie_eps: float = 1e-5, n_group: int = 1, topk_group: int = 1,
+                    group_topk: int = 2) -> RoutingReport:
+    """Indices slot for slot against the oracle, near-ties excused (see above).
+
+    With ``n_group`` > 1 the routing is group-limited; a differing choice is
+    valid when its kept groups and its experts are both near-top choices.
+    """
     idx = np.asarray(idx, dtype=np.int64)
     w = np.asarray(w, dtype=np.float64)
-    r = ref if ref is not None else moe.route(x, router_w, corr_bias, k, scale)
+    groups = dict(n_group=n_group, topk_group=topk_group, group_topk=group_topk)
+    r = ref if ref is not None else moe.route(x, router_w, corr_bias, k, scale, **groups)
     T, E = r.beta.shape
     forced = r.idx.copy()
     exact = (idx == r.idx).all(axis=1)
     invalid, excused = [], 0
-    if not exact.all():
-        kth = -np.sort(-r.beta, axis=1)[:, k - 1]
     for t in np.nonzero(~exact)[0]:
-        sel = idx[t]
-        ok = (len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E)
-        if ok:
-            b = r.beta[t]
-            chosen = b[sel]
-            rest = np.delete(b, sel)
-            ok = (chosen.min() >= kth[t] - tie_eps
-                  and (rest.size == 0 or rest.max() <= chosen.min() + tie_eps)
-                  and (np.diff(chosen) <= tie_eps).all())
-        if ok:
+        if _valid_choice(r.beta[t], idx[t], k, n_group, topk_group, group_topk, tie_eps):
             excused += 1
-            forced[t] = sel
+            forced[t] = idx[t]
         else:
             invalid.append(int(t))
     rf = moe.route(x, router_w, corr_bias, k, scale, force_idx=forced)

@@ -5,8 +5,9 @@ The layer runs in hand-written HIP kernels behind the C ABI of
 binding.  Build the library with ``python -m sparse_moe_transformer_glm_amd.build``.
 """
 from ._lib import (BF16, EHIP, EINVAL, EUNSUPPORTED, EWORKSPACE, F32, LIB_PATH, OK, STAGES,
-                   GlmMoeError, Trace, forward, lib, new_workspace, route, workspace_size)
+                   GlmMoeError, Options, Trace, dense_ffn, dense_workspace_size, forward, lib,
+                   new_workspace, options, route, workspace_size)
 
 __all__ = ["BF16", "EHIP", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "F32", "LIB_PATH", "OK",
-           "STAGES", "GlmMoeError", "Trace", "forward", "lib", "new_workspace", "route",
-           "workspace_size"]
+           "STAGES", "GlmMoeError", "Options", "Trace", "dense_ffn", "dense_workspace_size",
+           "forward", "lib", "new_workspace", "options", "route", "workspace_size"]

@@ -34,6 +34,13 @@ class Dims(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32)]
 
 
+class Options(ctypes.Structure):
+    """``glm_moe_options``: group-limited routing and the pre-norm block."""
+    _fields_ = [("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("group_topk", ctypes.c_int32), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("add_residual", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -47,12 +54,18 @@ def lib() -> ctypes.CDLL:
                 "`python -m sparse_moe_transformer_glm_amd.build` (gfx950 HIP library)")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        pd = ctypes.POINTER(Dims)
+        pd, po = ctypes.POINTER(Dims), ctypes.POINTER(Options)
         L.glm_moe_workspace_size.argtypes = [pd, i32, ctypes.POINTER(sz)]
+        L.glm_moe_workspace_size_ex.argtypes = [pd, po, i32, ctypes.POINTER(sz)]
         L.glm_moe_route.argtypes = [pd, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.glm_moe_route_ex.argtypes = [pd, po, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.glm_moe_forward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
                                       vp, sz, vp]
         L.glm_moe_forward_traced.argtypes = L.glm_moe_forward.argtypes + [vp]
+        L.glm_moe_forward_ex.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
+                                         vp, vp, vp, sz, vp, vp]
+        L.glm_moe_dense_workspace_size.argtypes = [pd, po, ctypes.POINTER(sz)]
+        L.glm_moe_dense_ffn.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, sz, vp]
         L.glm_moe_trace_create.argtypes = [ctypes.POINTER(vp), i32]
         L.glm_moe_trace_destroy.argtypes = [vp]
         L.glm_moe_trace_reset.argtypes = [vp]
@@ -62,9 +75,11 @@ def lib() -> ctypes.CDLL:
         L.glm_moe_last_error.argtypes = []
         L.glm_moe_last_error.restype = ctypes.c_char_p
         L.glm_moe_version.restype = i32
-        for name in ("glm_moe_workspace_size", "glm_moe_route", "glm_moe_forward",
-                     "glm_moe_forward_traced", "glm_moe_trace_create", "glm_moe_trace_destroy",
-                     "glm_moe_trace_reset", "glm_moe_trace_read"):
+        for name in ("glm_moe_workspace_size", "glm_moe_workspace_size_ex", "glm_moe_route",
+                     "glm_moe_route_ex", "glm_moe_forward", "glm_moe_forward_traced",
+                     "glm_moe_forward_ex", "glm_moe_dense_workspace_size", "glm_moe_dense_ffn",
+                     "glm_moe_trace_create", "glm_moe_trace_destroy", "glm_moe_trace_reset",
+                     "glm_moe_trace_read"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -90,11 +105,32 @@ def dims(T: int, D: int, E: int, F: int, Fs: int, dtype: torch.dtype) -> Dims:
     return Dims(T, D, E, F, Fs, c, c)
 
 
+def options(n_group: int = 1, topk_group: int = 1, group_topk: int = 0,
+            norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
+            residual: bool = False, D: Optional[int] = None) -> Options:
+    """Marshal the layer options (``norm_weight`` is a [D] float32 GPU tensor)."""
+    nw = 0
+    if norm_weight is not None:
+        nw = _ptr(norm_weight, "norm_weight", torch.float32, None if D is None else (D,))
+    return Options(int(n_group), int(topk_group), int(group_topk), nw or None, float(norm_eps),
+                   1 if residual else 0)
+
+
 def workspace_size(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
-                   dtype: torch.dtype = torch.bfloat16) -> int:
+                   dtype: torch.dtype = torch.bfloat16, opts: Optional[Options] = None) -> int:
     n = ctypes.c_size_t(0)
-    _check(lib().glm_moe_workspace_size(ctypes.byref(dims(T, D, E, F, Fs, dtype)), top_k,
-                                        ctypes.byref(n)), "glm_moe_workspace_size")
+    _check(lib().glm_moe_workspace_size_ex(ctypes.byref(dims(T, D, E, F, Fs, dtype)),
+                                           None if opts is None else ctypes.byref(opts), top_k,
+                                           ctypes.byref(n)), "glm_moe_workspace_size_ex")
+    return n.value
+
+
+def dense_workspace_size(T: int, D: int, F: int, dtype: torch.dtype = torch.bfloat16,
+                         opts: Optional[Options] = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().glm_moe_dense_workspace_size(ctypes.byref(dims(T, D, 0, 0, F, dtype)),
+                                              None if opts is None else ctypes.byref(opts),
+                                              ctypes.byref(n)), "glm_moe_dense_workspace_size")
     return n.value
 
 
@@ -116,32 +152,37 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def new_workspace(T, D, E, F, Fs, top_k, dtype, device=None) -> torch.Tensor:
-    n = workspace_size(T, D, E, F, Fs, top_k, dtype)
+def new_workspace(T, D, E, F, Fs, top_k, dtype, device=None,
+                  opts: Optional[Options] = None) -> torch.Tensor:
+    n = workspace_size(T, D, E, F, Fs, top_k, dtype, opts)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
 
 
 def route(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor, top_k: int,
           scale: float, workspace: Optional[torch.Tensor] = None,
           topk_idx: Optional[torch.Tensor] = None,
-          topk_w: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+          topk_w: Optional[torch.Tensor] = None, *, n_group: int = 1, topk_group: int = 1,
+          group_topk: int = 0, norm_weight: Optional[torch.Tensor] = None,
+          norm_eps: float = 1e-5) -> Tuple[torch.Tensor, torch.Tensor]:
     """Router only; returns (topk_idx [T, k] int32, topk_w [T, k] float32)."""
     T, D = x.shape
     E = router_w.shape[0]
     d = dims(T, D, E, 64, 64, x.dtype)
+    o = options(n_group, topk_group, group_topk, norm_weight, norm_eps, False, D)
     if topk_idx is None:
         topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
     if topk_w is None:
         topk_w = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = new_workspace(T, D, E, 64, 64, top_k, x.dtype, x.device)
-    st = lib().glm_moe_route(
-        ctypes.byref(d), _ptr(x, "x"), _ptr(router_w, "router_w", torch.float32, (E, D)),
+        workspace = new_workspace(T, D, E, 64, 64, top_k, x.dtype, x.device, o)
+    st = lib().glm_moe_route_ex(
+        ctypes.byref(d), ctypes.byref(o), _ptr(x, "x"),
+        _ptr(router_w, "router_w", torch.float32, (E, D)),
         _ptr(corr_bias, "corr_bias", torch.float32, (E,)), top_k, float(scale),
         _ptr(topk_idx, "topk_idx", torch.int32, (T, top_k)),
         _ptr(topk_w, "topk_w", torch.float32, (T, top_k)),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
-    _check(st, "glm_moe_route")
+    _check(st, "glm_moe_route_ex")
     return topk_idx, topk_w
 
 
@@ -181,22 +222,27 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
             top_k: int, scale: float, out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None,
             topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-            trace: Optional[Trace] = None) -> torch.Tensor:
+            trace: Optional[Trace] = None, *, n_group: int = 1, topk_group: int = 1,
+            group_topk: int = 0, norm_weight: Optional[torch.Tensor] = None,
+            norm_eps: float = 1e-5, residual: bool = False) -> torch.Tensor:
     """The whole MoE layer; returns ``out`` [T, D] float32.
 
-    Pass ``topk_idx`` / ``topk_w`` tensors to also receive the routing.
+    Pass ``topk_idx`` / ``topk_w`` tensors to also receive the routing.  With
+    ``norm_weight`` the layer runs on RMSNorm(x); ``residual`` adds x to the
+    output; ``n_group`` > 1 turns on group-limited routing.
     """
     T, D = x.shape
     E, F, _ = w1.shape
     Fs = shared_w1.shape[0]
     dt = x.dtype
     d = dims(T, D, E, F, Fs, dt)
+    o = options(n_group, topk_group, group_topk, norm_weight, norm_eps, residual, D)
     if out is None:
         out = torch.empty((T, D), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = new_workspace(T, D, E, F, Fs, top_k, dt, x.device)
-    args = (
-        ctypes.byref(d), _ptr(x, "x", dt, (T, D)),
+        workspace = new_workspace(T, D, E, F, Fs, top_k, dt, x.device, o)
+    st = lib().glm_moe_forward_ex(
+        ctypes.byref(d), ctypes.byref(o), _ptr(x, "x", dt, (T, D)),
         _ptr(router_w, "router_w", torch.float32, (E, D)),
         _ptr(corr_bias, "corr_bias", torch.float32, (E,)),
         _ptr(w1, "w1", dt, (E, F, D)), _ptr(w3, "w3", dt, (E, F, D)),
@@ -206,11 +252,31 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
         top_k, float(scale), _ptr(out, "out", torch.float32, (T, D)),
         _ptr(topk_idx, "topk_idx", torch.int32, (T, top_k)),
         _ptr(topk_w, "topk_w", torch.float32, (T, top_k)),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(),
+        None if trace is None else trace.handle)
+    _check(st, "glm_moe_forward_ex")
+    return out
+
+
+def dense_ffn(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, *,
+              norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
+              residual: bool = False) -> torch.Tensor:
+    """A dense SiLU-gated FFN on the same kernels; returns ``out`` [T, D] float32."""
+    T, D = x.shape
+    F = w1.shape[0]
+    dt = x.dtype
+    d = dims(T, D, 0, 0, F, dt)
+    o = options(1, 1, 0, norm_weight, norm_eps, residual, D)
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(dense_workspace_size(T, D, F, dt, o), 1), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().glm_moe_dense_ffn(
+        ctypes.byref(d), ctypes.byref(o), _ptr(x, "x", dt, (T, D)),
+        _ptr(w1, "w1", dt, (F, D)), _ptr(w3, "w3", dt, (F, D)), _ptr(w2, "w2", dt, (D, F)),
+        _ptr(out, "out", torch.float32, (T, D)),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
-    L = lib()
-    if trace is None:
-        st = L.glm_moe_forward(*args)
-    else:
-        st = L.glm_moe_forward_traced(*args, trace.handle)
-    _check(st, "glm_moe_forward")
+    _check(st, "glm_moe_dense_ffn")
     return out

@@ -45,8 +45,13 @@ hipError_t launch_router_logits_f32(const float* x, const float* router_w, float
 
 // Sum partials, sigmoid, biased top-k, renormalise and scale; per-64-token
 // tile expert membership masks.
+// Group-limited selection when n_group > 1 (keep the topk_group groups with
+// the largest sum of their group_topk best biased scores).
+struct GroupRouting {
+  int n_group, topk_group, group_topk;
+};
 hipError_t launch_router_topk(const float* partial, int ksplit, const float* corr_bias,
-                              int T, int E, int k, float scale,
+                              int T, int E, int k, float scale, GroupRouting gr,
                               int32_t* topk_idx, float* topk_w, uint64_t* masks,
                               hipStream_t s);
 
@@ -106,9 +111,16 @@ struct DownArgs {
 };
 hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s);
 
-// out[t] = Y[t][k] + sum_{j<k} Y[t][j]: the shared expert's output, then the
-// weighted routed outputs in slot order.
-hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, hipStream_t s);
+// out[t] = Y[t][k] + sum_{j<k} Y[t][j] (+ residual[t]): the shared expert's
+// output, then the weighted routed outputs in slot order, then the residual
+// stream when `residual` is non-null (bf16 or fp32 per res_bf16).
+hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, const void* residual,
+                          bool res_bf16, hipStream_t s);
+
+// Pre-norm block: out = h / sqrt(mean(h^2) + eps) * w per row, computed in
+// fp64 and rounded once to the activation dtype (bf16 or fp32).
+hipError_t launch_rmsnorm(const void* h, const float* w, void* out, int T, int D, float eps,
+                          bool bf16, hipStream_t s);
 
 // fp32 path (plain kernels; same data flow).
 struct F32Args {
@@ -119,6 +131,7 @@ struct F32Args {
   const float* sw1; const float* sw3; const float* sw2;
   const float* topk_w;
   float* H; float* Hs; float* Y; float* out;
+  const float* residual;       // nullable: added to out last
   int T, D, E, F, Fs, k;
 };
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t s);

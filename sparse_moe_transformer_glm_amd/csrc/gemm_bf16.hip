@@ -343,10 +343,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   }
 }
 
-// out[t][d] = Y[t][k][d] + Y[t][0][d] + ... + Y[t][k-1][d], four columns per thread.
+// out[t][d] = Y[t][k][d] + Y[t][0][d] + ... + Y[t][k-1][d] (+ residual[t][d]),
+// four columns per thread.
+template <int RES>  // 0: none, 1: bf16 residual, 2: fp32 residual
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       float* __restrict__ out, int T, int D,
-                                                      int k) {
+                                                      int k, const void* __restrict__ residual) {
   const int D4 = D / 4;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)T * D4) return;
@@ -356,6 +358,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < k; ++j) {
     const float4 u = y[(size_t)j * D4];
     v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+  }
+  if constexpr (RES == 1) {
+    const uint2 r = reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(residual) +
+                                                   (size_t)t * D)[c];
+    v.x += __uint_as_float(r.x << 16); v.y += __uint_as_float(r.x & 0xFFFF0000u);
+    v.z += __uint_as_float(r.y << 16); v.w += __uint_as_float(r.y & 0xFFFF0000u);
+  } else if constexpr (RES == 2) {
+    const float4 r = reinterpret_cast<const float4*>(static_cast<const float*>(residual) +
+                                                     (size_t)t * D)[c];
+    v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
   }
   reinterpret_cast<float4*>(out + (size_t)t * D)[c] = v;
 }
@@ -407,10 +419,14 @@ hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s) {
   return dispatch<DOWN>(sh, GateUpArgs{}, a, (unsigned)a.grid, s);
 }
 
-hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, hipStream_t s) {
+hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, const void* residual,
+                          bool res_bf16, hipStream_t s) {
   const size_t n = (size_t)T * (D / 4);
   if (n == 0) return hipSuccess;
-  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(Y, out, T, D, k);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (!residual) combine_kernel<0><<<grid, 256, 0, s>>>(Y, out, T, D, k, nullptr);
+  else if (res_bf16) combine_kernel<1><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
+  else combine_kernel<2><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
   return hipGetLastError();
 }
 

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void shared_combine_f32_kernel(F32Args a) {
   const int t = (int)(i / a.D), d = (int)(i % a.D);
   float v = dot(a.Hs + (size_t)t * a.Fs, a.sw2 + (size_t)d * a.Fs, a.Fs);
   for (int j = 0; j < a.k; ++j) v += a.Y[((size_t)t * (a.k + 1) + j) * a.D + d];
+  if (a.residual) v += a.residual[i];
   a.out[i] = v;
 }
 
@@ -80,6 +81,7 @@ hipError_t launch_gateup_f32(const F32Args& a, hipStream_t s) {
 }
 
 hipError_t launch_down_f32(const F32Args& a, hipStream_t s) {
+  if ((size_t)a.T * a.k * a.D == 0) return hipSuccess;
   down_f32_kernel<<<blocks((size_t)a.T * a.k * a.D), 256, 0, s>>>(a);
   return hipGetLastError();
 }

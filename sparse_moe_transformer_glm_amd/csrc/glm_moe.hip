@@ -1,11 +1,14 @@
 // C ABI of the GLM-5.2 MoE layer: argument checks, workspace plan and the
-// launch sequence router -> top-k -> scan -> scatter -> gate/up -> down ->
-// shared+combine, all on the caller's stream.
+// launch sequence [rmsnorm ->] router -> top-k -> scan -> scatter -> gate/up
+// -> down -> combine [+ residual], all on the caller's stream.  The dense
+// feed-forward entry runs the same kernels with the shared group only.
 #include "glm_moe.h"
 #include "common.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <new>
 #include <vector>
 
 using namespace glm;
@@ -29,11 +32,16 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int T, D, E, F, Fs, k;
   bool bf16;
+  bool dense;        // no routed experts: the shared group only
   int ntiles;        // 64-token routing tiles
   int ksplit, kchunk;
   GemmShape gu, dn;
   int gu_cap, dn_cap;
-  size_t partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
+  GroupRouting gr;
+  const float* norm_weight;
+  float norm_eps;
+  bool add_residual;
+  size_t xnorm, partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
       dn_desc, row_assign, H, Hs, Y;
   size_t total;
 };
@@ -44,36 +52,80 @@ int desc_cap(int A, int E, GemmShape s, int ncol_tiles) {
   return (int)(mt * ncol_tiles);
 }
 
-int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
+int check_options(const glm_moe_options* o, int E, int top_k, bool dense, Plan& P) {
+  P.gr = GroupRouting{1, 1, 2};
+  P.norm_weight = nullptr;
+  P.norm_eps = 0.f;
+  P.add_residual = false;
+  if (!o) return GLM_MOE_OK;
+  if (!dense && o->n_group > 1) {
+    const int ng = o->n_group;
+    if (ng > 64) return fail(GLM_MOE_EUNSUPPORTED, "n_group=%d > 64", ng);
+    if (E % ng) return fail(GLM_MOE_EINVAL, "E=%d is not a multiple of n_group=%d", E, ng);
+    const int gsz = E / ng;
+    const int gk = o->group_topk == 0 ? (gsz < 2 ? gsz : 2) : o->group_topk;
+    if (o->topk_group < 1 || o->topk_group > ng)
+      return fail(GLM_MOE_EINVAL, "topk_group=%d outside [1, %d]", o->topk_group, ng);
+    if (gk < 1 || gk > gsz)
+      return fail(GLM_MOE_EINVAL, "group_topk=%d outside [1, %d]", gk, gsz);
+    if (o->topk_group * gsz < top_k)
+      return fail(GLM_MOE_EINVAL, "topk_group*E/n_group=%d < top_k=%d", o->topk_group * gsz,
+                  top_k);
+    P.gr = GroupRouting{ng, o->topk_group, gk};
+  } else if (!dense && o->n_group < 0) {
+    return fail(GLM_MOE_EINVAL, "n_group=%d < 0", o->n_group);
+  }
+  if (o->norm_weight) {
+    if (!(o->norm_eps >= 0.f) || !std::isfinite(o->norm_eps))
+      return fail(GLM_MOE_EINVAL, "norm_eps must be finite and >= 0");
+    if (reinterpret_cast<uintptr_t>(o->norm_weight) & 15)
+      return fail(GLM_MOE_EINVAL, "norm_weight is not 16-byte aligned");
+    P.norm_weight = o->norm_weight;
+    P.norm_eps = o->norm_eps;
+  }
+  P.add_residual = o->add_residual != 0;
+  return GLM_MOE_OK;
+}
+
+int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, bool dense,
+              Plan* p) {
   if (!d) return fail(GLM_MOE_EINVAL, "dims is null");
-  if (d->T < 0 || d->D <= 0 || d->E <= 0 || d->F <= 0 || d->F_shared <= 0)
+  if (d->T < 0 || d->D <= 0 || d->F_shared <= 0 || (!dense && (d->E <= 0 || d->F <= 0)))
     return fail(GLM_MOE_EINVAL, "bad sizes T=%d D=%d E=%d F=%d F_shared=%d", d->T, d->D, d->E,
                 d->F, d->F_shared);
-  if (d->E > kMaxExperts)
+  if (!dense && d->E > kMaxExperts)
     return fail(GLM_MOE_EUNSUPPORTED, "E=%d exceeds %d experts", d->E, kMaxExperts);
-  const int kmax = d->E < kMaxTopK ? d->E : kMaxTopK;
-  if (top_k < 1 || top_k > kmax)
-    return fail(GLM_MOE_EINVAL, "top_k=%d outside [1, %d]", top_k, kmax);
+  if (!dense) {
+    const int kmax = d->E < kMaxTopK ? d->E : kMaxTopK;
+    if (top_k < 1 || top_k > kmax)
+      return fail(GLM_MOE_EINVAL, "top_k=%d outside [1, %d]", top_k, kmax);
+  }
   if (d->act_dtype != d->weight_dtype ||
       (d->act_dtype != GLM_MOE_F32 && d->act_dtype != GLM_MOE_BF16))
     return fail(GLM_MOE_EUNSUPPORTED, "dtype pair act=%d weight=%d (supported: f32/f32, bf16/bf16)",
                 d->act_dtype, d->weight_dtype);
   const bool bf16 = d->act_dtype == GLM_MOE_BF16;
-  if (bf16 && (d->D % 64 || d->F % 64 || d->F_shared % 64))
+  if (bf16 && (d->D % 64 || d->F_shared % 64 || (!dense && d->F % 64)))
     return fail(GLM_MOE_EUNSUPPORTED, "bf16 path needs D, F, F_shared multiples of 64 (D=%d F=%d Fs=%d)",
                 d->D, d->F, d->F_shared);
-  if ((long long)d->T * top_k > (1ll << 30))
+  if ((long long)d->T * (dense ? 1 : top_k) > (1ll << 30))
     return fail(GLM_MOE_EUNSUPPORTED, "T*top_k=%lld too large", (long long)d->T * top_k);
 
   Plan& P = *p;
-  P.T = d->T; P.D = d->D; P.E = d->E; P.F = d->F; P.Fs = d->F_shared; P.k = top_k;
+  int st = check_options(opts, d->E, top_k, dense, P);
+  if (st) return st;
+  P.dense = dense;
+  P.T = d->T; P.D = d->D; P.Fs = d->F_shared;
+  P.E = dense ? 0 : d->E;
+  P.F = dense ? 0 : d->F;
+  P.k = dense ? 0 : top_k;
   P.bf16 = bf16;
-  const int T = P.T, A = T * top_k;
+  const int T = P.T, A = T * P.k;
   P.ntiles = cdiv(T, kTokTile);
 
   if (bf16) {
     // enough (token tile, expert group, K slice) workgroups to cover the chip
-    const int base = cdiv(T, 64) * cdiv(P.E, 64);
+    const int base = cdiv(T, 64) * cdiv(P.E > 0 ? P.E : 1, 64);
     int ks = cdiv(512, base > 0 ? base : 1);
     const int ksteps = P.D / 64;
     if (ks > 24) ks = 24;
@@ -81,12 +133,15 @@ int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
     if (ks < 1) ks = 1;
     P.kchunk = cdiv(ksteps, ks) * 64;
     P.ksplit = cdiv(P.D, P.kchunk);
-    const double per_expert = (double)A / P.E;
-    P.gu = gemm_shape(per_expert, P.F % 128 == 0 && P.Fs % 128 == 0);
-    P.dn = gemm_shape(per_expert, P.D % 256 == 0);
-    // routed tiles, then the shared expert's tiles (group E)
-    P.gu_cap = desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN) + cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
-    P.dn_cap = desc_cap(A, P.E, P.dn, P.D / P.dn.BN) + cdiv(T, P.dn.BM) * (P.D / P.dn.BN);
+    const double per_group = dense ? (double)T : (double)A / P.E;
+    const bool wide_gu = (dense || P.F % 128 == 0) && P.Fs % 128 == 0;
+    P.gu = gemm_shape(per_group, wide_gu);
+    P.dn = gemm_shape(per_group, P.D % 256 == 0);
+    // routed tiles, then the shared (or dense) group's tiles (group E)
+    P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) +
+               cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
+    P.dn_cap = (dense ? 0 : desc_cap(A, P.E, P.dn, P.D / P.dn.BN)) +
+               cdiv(T, P.dn.BM) * (P.D / P.dn.BN);
   } else {
     P.ksplit = 1; P.kchunk = P.D;
     P.gu = P.dn = GemmShape{0, 0};
@@ -96,7 +151,8 @@ int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
   const size_t act = bf16 ? 2 : 4;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
-  P.partial = take((size_t)P.ksplit * T * P.E * 4);
+  P.xnorm = take(P.norm_weight ? (size_t)T * P.D * act : 0);
+  P.partial = take(dense ? 0 : (size_t)P.ksplit * T * P.E * 4);
   P.idx = take((size_t)A * 4);
   P.w = take((size_t)A * 4);
   P.masks = take((size_t)P.ntiles * P.E * 8);
@@ -110,7 +166,7 @@ int make_plan(const glm_moe_dims* d, int top_k, Plan* p) {
   P.row_assign = take((size_t)A * 4);
   P.H = take((size_t)A * P.F * act);
   P.Hs = take((size_t)T * P.Fs * act);
-  P.Y = take((size_t)T * (top_k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
+  P.Y = take((size_t)T * (P.k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
   P.total = T == 0 ? 0 : o;
   return GLM_MOE_OK;
 }
@@ -165,86 +221,42 @@ struct Recorder {
       return fail(GLM_MOE_EHIP, "%s: %s", #expr, hipGetErrorString(e_));          \
   } while (0)
 
-int run_router(const Plan& P, const void* x, const float* router_w, const float* corr_bias,
-               float scale, int32_t* idx, float* w, void* ws, hipStream_t s, Recorder& rec) {
+// RMSNorm of the residual stream into the workspace when requested; returns
+// the input the layer runs on.  (Timed as part of the router-logits stage.)
+int layer_input(const Plan& P, const void* x, void* ws, hipStream_t s, const void** xin) {
+  *xin = x;
+  if (P.norm_weight) {
+    void* xn = at<char>(ws, P.xnorm);
+    GLM_HIP(launch_rmsnorm(x, P.norm_weight, xn, P.T, P.D, P.norm_eps, P.bf16, s));
+    *xin = xn;
+  }
+  return GLM_MOE_OK;
+}
+
+int run_router(const Plan& P, const void* xin, const float* router_w, void* ws, hipStream_t s) {
   float* partial = at<float>(ws, P.partial);
   uint64_t* masks = at<uint64_t>(ws, P.masks);
-  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
   if (P.bf16)
-    GLM_HIP(launch_router_logits_bf16(static_cast<const bf16_t*>(x), router_w, partial, P.T, P.D,
-                                      P.E, P.ksplit, P.kchunk, masks, s));
+    GLM_HIP(launch_router_logits_bf16(static_cast<const bf16_t*>(xin), router_w, partial, P.T,
+                                      P.D, P.E, P.ksplit, P.kchunk, masks, s));
   else
-    GLM_HIP(launch_router_logits_f32(static_cast<const float*>(x), router_w, partial, P.T, P.D,
-                                     P.E, masks, s));
-  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
-  GLM_HIP(launch_router_topk(partial, P.ksplit, corr_bias, P.T, P.E, P.k, scale, idx, w, masks, s));
+    GLM_HIP(launch_router_logits_f32(static_cast<const float*>(xin), router_w, partial, P.T,
+                                     P.D, P.E, masks, s));
   return GLM_MOE_OK;
 }
 
-int check_route_args(const void* x, const float* router_w, const float* corr_bias) {
-  int st;
-  if ((st = check_ptr(x, "x"))) return st;
-  if ((st = check_ptr(router_w, "router_w"))) return st;
-  if ((st = check_ptr(corr_bias, "corr_bias"))) return st;
+int run_topk(const Plan& P, const float* corr_bias, float scale, int32_t* idx, float* w,
+             void* ws, hipStream_t s) {
+  GLM_HIP(launch_router_topk(at<float>(ws, P.partial), P.ksplit, corr_bias, P.T, P.E, P.k, scale,
+                             P.gr, idx, w, at<uint64_t>(ws, P.masks), s));
   return GLM_MOE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes) {
-  if (!bytes) return fail(GLM_MOE_EINVAL, "bytes is null");
-  Plan P;
-  int st = make_plan(d, top_k, &P);
-  if (st) return st;
-  *bytes = P.total;
-  return GLM_MOE_OK;
-}
-
-int glm_moe_route(const glm_moe_dims* d, const void* x, const float* router_w,
-                  const float* corr_bias, int top_k, float scale, int32_t* topk_idx,
-                  float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Plan P;
-  int st = make_plan(d, top_k, &P);
-  if (st) return st;
-  if (P.T == 0) return GLM_MOE_OK;
-  if ((st = check_route_args(x, router_w, corr_bias))) return st;
-  if ((st = check_ptr(topk_idx, "topk_idx"))) return st;
-  if ((st = check_ptr(topk_w, "topk_w"))) return st;
-  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
-  Recorder rec(nullptr, stream);
-  return run_router(P, x, router_w, corr_bias, scale, topk_idx, topk_w, workspace, stream, rec);
-}
-
-int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* router_w,
-                           const float* corr_bias, const void* w1, const void* w3,
-                           const void* w2, const void* shared_w1, const void* shared_w3,
-                           const void* shared_w2, int top_k, float scale, float* out,
-                           int32_t* topk_idx_out, float* topk_w_out, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream, glm_moe_trace* trace) {
-  Plan P;
-  int st = make_plan(d, top_k, &P);
-  if (st) return st;
-  if (P.T == 0) return GLM_MOE_OK;
-  if ((st = check_route_args(x, router_w, corr_bias))) return st;
-  if ((st = check_ptr(w1, "w1")) || (st = check_ptr(w3, "w3")) || (st = check_ptr(w2, "w2")) ||
-      (st = check_ptr(shared_w1, "shared_w1")) || (st = check_ptr(shared_w3, "shared_w3")) ||
-      (st = check_ptr(shared_w2, "shared_w2")) || (st = check_ptr(out, "out")))
-    return st;
-  if (topk_idx_out && misaligned(topk_idx_out))
-    return fail(GLM_MOE_EINVAL, "topk_idx_out is not 16-byte aligned");
-  if (topk_w_out && misaligned(topk_w_out))
-    return fail(GLM_MOE_EINVAL, "topk_w_out is not 16-byte aligned");
-  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
-
-  void* ws = workspace;
-  hipStream_t s = stream;
-  Recorder rec(trace, s);
-  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, P.idx);
-  float* wts = topk_w_out ? topk_w_out : at<float>(ws, P.w);
-  if ((st = run_router(P, x, router_w, corr_bias, scale, idx, wts, ws, s, rec))) return st;
-
+// Everything after the routing: permutation, grouped GEMMs, combine.
+int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, float* wts,
+                const void* w1, const void* w3, const void* w2, const void* shared_w1,
+                const void* shared_w3, const void* shared_w2, float* out, void* ws,
+                hipStream_t s, Recorder& rec) {
   uint64_t* masks = at<uint64_t>(ws, P.masks);
   int32_t* tile_base = at<int32_t>(ws, P.tile_base);
   int32_t* counts = at<int32_t>(ws, P.counts);
@@ -255,6 +267,7 @@ int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* ro
   TileDesc* dn_desc = at<TileDesc>(ws, P.dn_desc);
   int32_t* row_assign = at<int32_t>(ws, P.row_assign);
   float* Y = at<float>(ws, P.Y);
+  const void* residual = P.add_residual ? x : nullptr;
 
   ScanParams sp;
   sp.T = P.T; sp.E = P.E; sp.k = P.k; sp.F = P.F; sp.Fs = P.Fs; sp.D = P.D;
@@ -266,11 +279,11 @@ int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* ro
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCAN));
   GLM_HIP(launch_scan(masks, sp, counts, offsets, tile_base, gu_desc, gu_count, dn_desc, dn_count, s));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));
-  GLM_HIP(launch_scatter(idx, masks, tile_base, P.T, P.E, P.k, row_assign, s));
+  if (!P.dense) GLM_HIP(launch_scatter(idx, masks, tile_base, P.T, P.E, P.k, row_assign, s));
 
   if (P.bf16) {
     GateUpArgs ga{};
-    ga.x = static_cast<const bf16_t*>(x);
+    ga.x = static_cast<const bf16_t*>(xin);
     ga.row_assign = row_assign; ga.offsets = offsets;
     ga.w1 = static_cast<const bf16_t*>(w1); ga.w3 = static_cast<const bf16_t*>(w3);
     ga.sw1 = static_cast<const bf16_t*>(shared_w1); ga.sw3 = static_cast<const bf16_t*>(shared_w3);
@@ -291,10 +304,10 @@ int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* ro
     GLM_HIP(launch_down_bf16(da, P.dn, s));
 
     GLM_HIP(rec.mark(GLM_MOE_STAGE_SHARED_COMBINE));
-    GLM_HIP(launch_combine(Y, out, P.T, P.D, P.k, s));
+    GLM_HIP(launch_combine(Y, out, P.T, P.D, P.k, residual, true, s));
   } else {
     F32Args fa{};
-    fa.x = static_cast<const float*>(x);
+    fa.x = static_cast<const float*>(xin);
     fa.row_assign = row_assign; fa.offsets = offsets;
     fa.w1 = static_cast<const float*>(w1); fa.w3 = static_cast<const float*>(w3);
     fa.w2 = static_cast<const float*>(w2);
@@ -302,6 +315,7 @@ int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* ro
     fa.sw2 = static_cast<const float*>(shared_w2);
     fa.topk_w = wts;
     fa.H = at<float>(ws, P.H); fa.Hs = at<float>(ws, P.Hs); fa.Y = Y; fa.out = out;
+    fa.residual = static_cast<const float*>(residual);
     fa.T = P.T; fa.D = P.D; fa.E = P.E; fa.F = P.F; fa.Fs = P.Fs; fa.k = P.k;
     GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
     GLM_HIP(launch_gateup_f32(fa, s));
@@ -314,15 +328,141 @@ int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* ro
   return GLM_MOE_OK;
 }
 
+int check_route_args(const void* x, const float* router_w, const float* corr_bias) {
+  int st;
+  if ((st = check_ptr(x, "x"))) return st;
+  if ((st = check_ptr(router_w, "router_w"))) return st;
+  if ((st = check_ptr(corr_bias, "corr_bias"))) return st;
+  return GLM_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int glm_moe_workspace_size_ex(const glm_moe_dims* d, const glm_moe_options* opts, int top_k,
+                              size_t* bytes) {
+  if (!bytes) return fail(GLM_MOE_EINVAL, "bytes is null");
+  Plan P;
+  int st = make_plan(d, top_k, opts, false, &P);
+  if (st) return st;
+  *bytes = P.total;
+  return GLM_MOE_OK;
+}
+
+int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes) {
+  return glm_moe_workspace_size_ex(d, nullptr, top_k, bytes);
+}
+
+int glm_moe_route_ex(const glm_moe_dims* d, const glm_moe_options* opts, const void* x,
+                     const float* router_w, const float* corr_bias, int top_k, float scale,
+                     int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  Plan P;
+  int st = make_plan(d, top_k, opts, false, &P);
+  if (st) return st;
+  if (P.T == 0) return GLM_MOE_OK;
+  if ((st = check_route_args(x, router_w, corr_bias))) return st;
+  if ((st = check_ptr(topk_idx, "topk_idx"))) return st;
+  if ((st = check_ptr(topk_w, "topk_w"))) return st;
+  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+  const void* xin;
+  if ((st = layer_input(P, x, workspace, stream, &xin))) return st;
+  if ((st = run_router(P, xin, router_w, workspace, stream))) return st;
+  return run_topk(P, corr_bias, scale, topk_idx, topk_w, workspace, stream);
+}
+
+int glm_moe_route(const glm_moe_dims* d, const void* x, const float* router_w,
+                  const float* corr_bias, int top_k, float scale, int32_t* topk_idx,
+                  float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return glm_moe_route_ex(d, nullptr, x, router_w, corr_bias, top_k, scale, topk_idx, topk_w,
+                          workspace, workspace_bytes, stream);
+}
+
+int glm_moe_forward_ex(const glm_moe_dims* d, const glm_moe_options* opts, const void* x,
+                       const float* router_w, const float* corr_bias, const void* w1,
+                       const void* w3, const void* w2, const void* shared_w1,
+                       const void* shared_w3, const void* shared_w2, int top_k, float scale,
+                       float* out, int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, glm_moe_trace* trace) {
+  Plan P;
+  int st = make_plan(d, top_k, opts, false, &P);
+  if (st) return st;
+  if (P.T == 0) return GLM_MOE_OK;
+  if ((st = check_route_args(x, router_w, corr_bias))) return st;
+  if ((st = check_ptr(w1, "w1")) || (st = check_ptr(w3, "w3")) || (st = check_ptr(w2, "w2")) ||
+      (st = check_ptr(shared_w1, "shared_w1")) || (st = check_ptr(shared_w3, "shared_w3")) ||
+      (st = check_ptr(shared_w2, "shared_w2")) || (st = check_ptr(out, "out")))
+    return st;
+  if (topk_idx_out && misaligned(topk_idx_out))
+    return fail(GLM_MOE_EINVAL, "topk_idx_out is not 16-byte aligned");
+  if (topk_w_out && misaligned(topk_w_out))
+    return fail(GLM_MOE_EINVAL, "topk_w_out is not 16-byte aligned");
+  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+
+  void* ws = workspace;
+  hipStream_t s = stream;
+  Recorder rec(trace, s);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, P.idx);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, P.w);
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
+  const void* xin;
+  if ((st = layer_input(P, x, ws, s, &xin))) return st;
+  if ((st = run_router(P, xin, router_w, ws, s))) return st;
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
+  if ((st = run_topk(P, corr_bias, scale, idx, wts, ws, s))) return st;
+  return run_experts(P, x, xin, idx, wts, w1, w3, w2, shared_w1, shared_w3, shared_w2, out, ws,
+                     s, rec);
+}
+
+int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* router_w,
+                           const float* corr_bias, const void* w1, const void* w3,
+                           const void* w2, const void* shared_w1, const void* shared_w3,
+                           const void* shared_w2, int top_k, float scale, float* out,
+                           int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, glm_moe_trace* trace) {
+  return glm_moe_forward_ex(d, nullptr, x, router_w, corr_bias, w1, w3, w2, shared_w1, shared_w3,
+                            shared_w2, top_k, scale, out, topk_idx_out, topk_w_out, workspace,
+                            workspace_bytes, stream, trace);
+}
+
 int glm_moe_forward(const glm_moe_dims* d, const void* x, const float* router_w,
                     const float* corr_bias, const void* w1, const void* w3, const void* w2,
                     const void* shared_w1, const void* shared_w3, const void* shared_w2,
                     int top_k, float scale, float* out, int32_t* topk_idx_out,
                     float* topk_w_out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  return glm_moe_forward_traced(d, x, router_w, corr_bias, w1, w3, w2, shared_w1, shared_w3,
-                                shared_w2, top_k, scale, out, topk_idx_out, topk_w_out,
-                                workspace, workspace_bytes, stream, nullptr);
+  return glm_moe_forward_ex(d, nullptr, x, router_w, corr_bias, w1, w3, w2, shared_w1, shared_w3,
+                            shared_w2, top_k, scale, out, topk_idx_out, topk_w_out, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+int glm_moe_dense_workspace_size(const glm_moe_dims* d, const glm_moe_options* opts,
+                                 size_t* bytes) {
+  if (!bytes) return fail(GLM_MOE_EINVAL, "bytes is null");
+  Plan P;
+  int st = make_plan(d, 0, opts, true, &P);
+  if (st) return st;
+  *bytes = P.total;
+  return GLM_MOE_OK;
+}
+
+int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* opts, const void* x,
+                      const void* w1, const void* w3, const void* w2, float* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan P;
+  int st = make_plan(d, 0, opts, true, &P);
+  if (st) return st;
+  if (P.T == 0) return GLM_MOE_OK;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(w1, "w1")) || (st = check_ptr(w3, "w3")) ||
+      (st = check_ptr(w2, "w2")) || (st = check_ptr(out, "out")))
+    return st;
+  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+  Recorder rec(nullptr, stream);
+  const void* xin;
+  if ((st = layer_input(P, x, workspace, stream, &xin))) return st;
+  return run_experts(P, x, xin, nullptr, nullptr, nullptr, nullptr, nullptr, w1, w3, w2, out,
+                     workspace, stream, rec);
 }
 
 int glm_moe_trace_create(glm_moe_trace** trace, int max_calls) {
@@ -389,6 +529,6 @@ const char* glm_moe_status_string(int status) {
 
 const char* glm_moe_last_error(void) { return g_err; }
 
-int glm_moe_version(void) { return 100; }
+int glm_moe_version(void) { return 200; }
 
 }  // extern "C"

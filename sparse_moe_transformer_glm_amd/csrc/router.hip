@@ -136,28 +136,87 @@ __device__ inline float sum_partials(const float* p, size_t stride, int ksplit) 
 // keys (biased score, then lower index).  Each selection also sets the token's
 // bit in masks[token / 64][expert] (an OR, so the result does not depend on
 // the order of the atomics); the logits kernel has zeroed the masks.
+// Wave-wide maximum of 64-bit keys.
+__device__ inline unsigned long long wave_max(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Group-limited routing: experts form n_group consecutive groups; a group
+// scores the sum (fp32, largest first) of its group_topk best biased scores;
+// the token keeps the topk_group best groups (ties: lower group) and the keys
+// of experts outside them are cleared.
+__device__ inline void restrict_to_groups(unsigned long long (&key)[4], const float (&beta)[4],
+                                          int lane, int E, GroupRouting gr) {
+  const int gsz = E / gr.n_group;
+  float my_gscore = 0.f;  // lane g < n_group holds group g's score
+  for (int g = 0; g < gr.n_group; ++g) {
+    unsigned long long gk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) gk[c] = ((lane + 64 * c) / gsz == g) ? key[c] : 0ull;
+    float sum = 0.f;
+    for (int r = 0; r < gr.group_topk; ++r) {
+      unsigned long long best = gk[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) best = gk[c] > best ? gk[c] : best;
+      best = wave_max(best);
+      const int es = (int)(~(uint32_t)best);
+      const int src = es & 63, cs = es >> 6;
+      float mine = beta[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) mine = (cs == c) ? beta[c] : mine;
+      sum += __shfl(mine, src, 64);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (lane == src && cs == c) gk[c] = 0ull;
+    }
+    if (lane == g) my_gscore = sum;
+  }
+  unsigned long long gkey = lane < gr.n_group
+      ? ((unsigned long long)ordered_bits(my_gscore) << 32) | (uint32_t)(~lane) : 0ull;
+  unsigned long long keep = 0ull;  // bit g: group g kept
+  for (int r = 0; r < gr.topk_group; ++r) {
+    const unsigned long long best = wave_max(gkey);
+    const int gs = (int)(~(uint32_t)best);
+    keep |= 1ull << gs;
+    if (lane == gs) gkey = 0ull;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    if (e < E && !((keep >> (e / gsz)) & 1ull)) key[c] = 0ull;
+  }
+}
+
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ partial, int ksplit, const float* __restrict__ bias,
-    int T, int E, int k, float scale, int32_t* __restrict__ idx_out,
+    int T, int E, int k, float scale, GroupRouting gr, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out, unsigned long long* __restrict__ masks) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const size_t stride = (size_t)T * E;
-  float sig[4];
+  float sig[4], beta[4];
   unsigned long long key[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
     sig[c] = 0.f;
+    beta[c] = 0.f;
     key[c] = 0ull;
     if (e < E) {
       const float z = sum_partials(partial + (size_t)t * E + e, stride, ksplit);
       const float sg = 1.0f / (1.0f + expf(-z));
       sig[c] = sg;
-      key[c] = ((unsigned long long)ordered_bits(sg + bias[e]) << 32) | (uint32_t)(~e);
+      beta[c] = sg + bias[e];
+      key[c] = ((unsigned long long)ordered_bits(beta[c]) << 32) | (uint32_t)(~e);
     }
   }
+  if (gr.n_group > 1) restrict_to_groups(key, beta, lane, E, gr);
   unsigned long long* tmask = masks + (size_t)(t / kTokTile) * E;
   const unsigned long long bit = 1ull << (t % kTokTile);
   float ssum = 0.f, my_sig = 0.f;
@@ -166,11 +225,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     unsigned long long best = key[0];
 #pragma unroll
     for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned long long o = __shfl_xor(best, off, 64);
-      best = o > best ? o : best;
-    }
+    best = wave_max(best);
     const int es = (int)(~(uint32_t)best);
     const int src = es & 63, cs = es >> 6;
     float mine = sig[0];
@@ -215,9 +270,9 @@ hipError_t launch_router_logits_f32(const float* x, const float* router_w, float
 }
 
 hipError_t launch_router_topk(const float* partial, int ksplit, const float* corr_bias, int T,
-                              int E, int k, float scale, int32_t* topk_idx, float* topk_w,
-                              uint64_t* masks, hipStream_t s) {
-  router_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(partial, ksplit, corr_bias, T, E, k, scale,
+                              int E, int k, float scale, GroupRouting gr, int32_t* topk_idx,
+                              float* topk_w, uint64_t* masks, hipStream_t s) {
+  router_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(partial, ksplit, corr_bias, T, E, k, scale, gr,
                                                topk_idx, topk_w,
                                                reinterpret_cast<unsigned long long*>(masks));
   return hipGetLastError();

@@ -167,3 +167,127 @@ def test_trace_argument_checks():
     assert L.glm_moe_trace_create(ctypes.byref(h), 0) == glm.EINVAL
     assert L.glm_moe_trace_reset(None) == glm.EINVAL
     assert L.glm_moe_trace_destroy(None) == glm.OK
+
+
+# ----------------------------------------------------------- options, dense
+
+from sparse_moe_transformer_glm_amd._lib import Options  # noqa: E402
+
+
+def _ws_ex(dims, k, opts, dt=glm.BF16):
+    n = ctypes.c_size_t(0)
+    st = glm.lib().glm_moe_workspace_size_ex(ctypes.byref(Dims(*dims, dt, dt)),
+                                             None if opts is None else ctypes.byref(opts), k,
+                                             ctypes.byref(n))
+    return st, n.value
+
+
+GLM = (64, 6144, 256, 2048, 2048)
+
+
+def test_workspace_ex_defaults_match_plain():
+    assert _ws_ex(GLM, 8, None) == _ws(*GLM, 8)
+    assert _ws_ex(GLM, 8, Options()) == _ws(*GLM, 8)
+    assert _ws_ex(GLM, 8, Options(8, 4, 2, None, 1e-5, 1)) == _ws(*GLM, 8)
+
+
+def test_workspace_ex_norm_holds_the_normalised_input():
+    _, plain = _ws(*GLM, 8)
+    st, n = _ws_ex(GLM, 8, Options(1, 1, 0, FAKE, 1e-5, 0))
+    assert st == glm.OK and n == plain + 64 * 6144 * 2
+    st, n = _ws_ex((64, 128, 8, 64, 64), 2, Options(1, 1, 0, FAKE, 1e-5, 0), glm.F32)
+    _, p32 = _ws(64, 128, 8, 64, 64, 2, glm.F32)
+    assert st == glm.OK and n == p32 + 64 * 128 * 4
+
+
+@pytest.mark.parametrize("opts,k,code", [
+    (Options(65, 1, 2, None, 0.0, 0), 8, glm.EUNSUPPORTED),   # > 64 groups
+    (Options(3, 1, 2, None, 0.0, 0), 8, glm.EINVAL),          # E % n_group
+    (Options(-2, 1, 2, None, 0.0, 0), 8, glm.EINVAL),         # negative n_group
+    (Options(8, 0, 2, None, 0.0, 0), 8, glm.EINVAL),          # topk_group < 1
+    (Options(8, 9, 2, None, 0.0, 0), 8, glm.EINVAL),          # topk_group > n_group
+    (Options(8, 4, 33, None, 0.0, 0), 8, glm.EINVAL),         # group_topk > group size
+    (Options(8, 4, -1, None, 0.0, 0), 8, glm.EINVAL),         # group_topk < 0
+    (Options(64, 1, 2, None, 0.0, 0), 8, glm.EINVAL),         # kept experts (4) < top_k
+    (Options(1, 1, 0, FAKE, -1.0, 0), 8, glm.EINVAL),         # eps < 0
+    (Options(1, 1, 0, FAKE, float("nan"), 0), 8, glm.EINVAL), # eps NaN
+    (Options(1, 1, 0, FAKE, float("inf"), 0), 8, glm.EINVAL), # eps inf
+    (Options(1, 1, 0, FAKE + 4, 1e-5, 0), 8, glm.EINVAL),     # misaligned norm weight
+])
+def test_invalid_options(opts, k, code):
+    st, _ = _ws_ex(GLM, k, opts)
+    assert st == code
+    assert glm.lib().glm_moe_last_error()
+
+
+def test_valid_group_options():
+    for o in (Options(8, 4, 2, None, 0.0, 0), Options(64, 2, 1, None, 0.0, 0),
+              Options(1, 0, 0, None, 0.0, 0), Options(0, 0, 0, None, 0.0, 0),
+              Options(8, 1, 0, None, 0.0, 0), Options(256, 1, 1, None, 0.0, 0)):
+        st, _ = _ws_ex((64, 128, 64 if o.n_group <= 64 else 256, 64, 64), 1, o)
+        assert st == (glm.OK if o.n_group <= 64 else glm.EUNSUPPORTED), (o.n_group, st)
+
+
+def _forward_ex(d, opts, k, ptrs, ws=0, ws_bytes=0):
+    return glm.lib().glm_moe_forward_ex(ctypes.byref(d), opts and ctypes.byref(opts), *ptrs[:9],
+                                        k, 1.0, ptrs[9], None, None, ws, ws_bytes, None, None)
+
+
+def test_forward_ex_checks_like_forward():
+    d = Dims(64, 128, 8, 64, 64, glm.BF16, glm.BF16)
+    o = Options(4, 2, 2, None, 0.0, 1)
+    good = [FAKE] * 10
+    for i in range(10):
+        p = list(good)
+        p[i] = 0
+        assert _forward_ex(d, o, 2, p) == glm.EINVAL
+    _, need = _ws_ex((64, 128, 8, 64, 64), 2, o)
+    assert _forward_ex(d, o, 2, good, FAKE, need - 1) == glm.EWORKSPACE
+    assert _forward_ex(d, Options(3, 1, 2, None, 0.0, 0), 2, good, FAKE, need) == glm.EINVAL
+    assert _forward_ex(Dims(0, 128, 8, 64, 64, glm.BF16, glm.BF16), o, 2, [0] * 10) == glm.OK
+
+
+def test_route_ex_checks_options():
+    L = glm.lib()
+    d = Dims(64, 128, 8, 64, 64, glm.BF16, glm.BF16)
+    bad = Options(8, 9, 2, None, 0.0, 0)
+    assert L.glm_moe_route_ex(ctypes.byref(d), ctypes.byref(bad), FAKE, FAKE, FAKE, 2, 1.0, FAKE,
+                              FAKE, FAKE, 1 << 30, None) == glm.EINVAL
+
+
+def _dense_ws(T, D, Fs, opts=None, dt=glm.BF16, E=0, F=0):
+    n = ctypes.c_size_t(0)
+    st = glm.lib().glm_moe_dense_workspace_size(ctypes.byref(Dims(T, D, E, F, Fs, dt, dt)),
+                                                opts and ctypes.byref(opts), ctypes.byref(n))
+    return st, n.value
+
+
+def test_dense_workspace():
+    st, n = _dense_ws(4096, 6144, 12288)
+    assert st == glm.OK
+    # hidden activations [T][F] bf16 and the fp32 output staging [T][D]
+    assert n >= 4096 * 12288 * 2 + 4096 * 6144 * 4
+    # E and F are ignored; grouping options too
+    assert _dense_ws(4096, 6144, 12288, E=7, F=3) == (glm.OK, n)
+    assert _dense_ws(4096, 6144, 12288, Options(3, 9, 99, None, 0.0, 1)) == (glm.OK, n)
+    assert _dense_ws(0, 6144, 12288) == (glm.OK, 0)
+    assert _dense_ws(64, 6144, 100)[0] == glm.EUNSUPPORTED
+    assert _dense_ws(64, 6144, 0)[0] == glm.EINVAL
+    assert _dense_ws(64, 6144, 100, dt=glm.F32)[0] == glm.OK
+
+
+def test_dense_argument_checks():
+    L = glm.lib()
+    d = Dims(64, 128, 0, 0, 64, glm.BF16, glm.BF16)
+    _, need = _dense_ws(64, 128, 64)
+    good = [FAKE] * 5
+    for i in range(5):
+        p = list(good)
+        p[i] = 0
+        assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *p, FAKE, need, None) == glm.EINVAL
+        p[i] = FAKE + 2
+        assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *p, FAKE, need, None) == glm.EINVAL
+    assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *good, FAKE, need - 1,
+                               None) == glm.EWORKSPACE
+    d0 = Dims(0, 128, 0, 0, 64, glm.BF16, glm.BF16)
+    assert L.glm_moe_dense_ffn(ctypes.byref(d0), None, 0, 0, 0, 0, 0, 0, 0, None) == glm.OK

@@ -297,3 +297,41 @@ def test_glm_shape(glm_layer, name, n_sample):
         sample = _sample(L.w.T, n_sample, extra=near[:4])
     check(L, out, idx, wt, sample=sample, label=name, ref=ref)
     log(f"{name}: checked in {time.time() - t0:.1f}s")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_glm_shape_block_with_group_routing(glm_layer):
+    """GLM-5.2 shape, decode batch, with the pre-norm block around the layer
+    (RMSNorm in, residual add out) and group-limited routing (8 groups of 32,
+    4 kept, scale 1.0)."""
+    L, dev = _glm_case(glm_layer, "glm_decode")
+    w = L.w
+    h, nw = wl.make_hidden(w), wl.make_norm_weight(w)
+    groups = dict(n_group=8, topk_group=4, group_topk=2)
+    eps, scale = 1e-5, 1.0
+    T = w.T
+    idx = torch.full((T, w.k), -1, dtype=torch.int32, device="cuda")
+    wt = torch.full((T, w.k), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((T, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    a = list(dev.args())
+    a[0] = to_device(h)
+    glm.forward(*a, w.k, scale, out=out, topk_idx=idx, topk_w=wt, norm_weight=to_device(nw),
+                norm_eps=eps, residual=True, **groups)
+    torch.cuda.synchronize()
+    out, idx, wt = out.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy()
+    xn = oracle.round_bf16(oracle.rmsnorm(h, nw, eps))
+    rep = parity.compare_routing(idx, wt, xn, L.router_w, L.corr_bias, w.k, scale, **groups)
+    assert rep.ok and rep.max_weight_err <= parity.WEIGHT_TOL
+    plain = oracle.route(xn, L.router_w, L.corr_bias, w.k, scale)
+    assert (plain.idx != rep.forced_idx).any()
+    ref, _ = oracle.block_ffn(
+        h, nw, eps, "bf16",
+        lambda x: oracle.forward(x, L.router_w, L.corr_bias,
+                                 lambda e: (L.w1[e], L.w3[e], L.w2[e]), (L.sw1, L.sw3, L.sw2),
+                                 w.k, scale, force_idx=rep.forced_idx))
+    base = oracle.decode(h)
+    o = parity.compare_output(out - base, ref - base)
+    log(f"glm block+groups: exact={rep.exact} near-tie={rep.excused} ffn max/rms={o.max_rel:.3e} "
+        f"mean/rms={o.mean_rel:.3e}")
+    assert o.max_rel <= parity.BF16_MAX_REL and o.mean_rel <= parity.BF16_MEAN_REL

@@ -14,13 +14,17 @@ Recipe (every stream is independent and addressable):
 
 * stream ids: ``SeedSequence([seed, tensor_id, expert_id])``;
   tensor ids 0 x, 1 router_w, 2 corr_bias, 3 w1, 4 w3, 5 w2, 6 shared_w1,
-  7 shared_w3, 8 shared_w2.
+  7 shared_w3, 8 shared_w2, 9 norm_weight, 10 residual stream h, 11-13 the
+  dense FFN's w1, w3, w2.
 * draws: ``standard_normal(float32) * float32(std)``; bf16 tensors are the
   RNE rounding of that fp32 value.
 * x ~ N(0, 1); router_w ~ N(0, 1/D); w1, w3 ~ N(0, 1/D); w2 ~ N(0, 1/F);
   shared likewise with F_s.  (The variance reading of ``N(0, 1/fan_in)``.)
 * corr_bias ~ N(0, bias_std) (the std reading); the skewed workloads then set
   the first ``hot_count`` entries to ``hot_value``.
+* Pre-norm block: h ~ N(0, 3^2) (a residual stream larger than unit scale, so
+  the norm is not near the identity); norm_weight = 1 + N(0, 0.1^2).
+* Dense FFN of width F_d: w1, w3 ~ N(0, 1/D), w2 ~ N(0, 1/F_d).
 * The layer weights (router, routed and shared experts) are seeded by
   ``weight_seed``; the GLM-shape workloads share one weight set, i.e. one
   layer seen with different token batches and bias regimes.  ``x`` and
@@ -35,7 +39,8 @@ from typing import Iterator, Optional, Tuple
 
 import numpy as np
 
-TID_X, TID_RW, TID_BIAS, TID_W1, TID_W3, TID_W2, TID_SW1, TID_SW3, TID_SW2 = range(9)
+(TID_X, TID_RW, TID_BIAS, TID_W1, TID_W3, TID_W2, TID_SW1, TID_SW3, TID_SW2, TID_NORM, TID_H,
+ TID_DW1, TID_DW3, TID_DW2) = range(14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +65,11 @@ class Workload:
 
 
 GLM_WEIGHT_SEED = 1000
+# Width of the leading dense FFN layers.  The pages give the count (three) but
+# not the width; this stand-in is 9 x 2048, the routed plus shared width one
+# token passes through in a MoE layer, so a dense layer does the same work per
+# token.
+GLM_DENSE_WIDTH = 18432
 
 WORKLOADS = {
     # tiny fp32 layer (parity at 1e-5)
@@ -151,6 +161,27 @@ def make_shared(w: Workload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     w1 = normal_f32(w.weight_seed, TID_SW1, 0, (w.Fs, w.D), s_in)
     w3 = normal_f32(w.weight_seed, TID_SW3, 0, (w.Fs, w.D), s_in)
     w2 = normal_f32(w.weight_seed, TID_SW2, 0, (w.D, w.Fs), s_out)
+    return _encode(w1, w.dtype), _encode(w3, w.dtype), _encode(w2, w.dtype)
+
+
+def make_norm_weight(w: Workload) -> np.ndarray:
+    """fp32 [D]: RMSNorm weight of the block, 1 + N(0, 0.1^2)."""
+    return (np.float32(1.0) + normal_f32(w.weight_seed, TID_NORM, 0, (w.D,), 0.1)).astype(
+        np.float32)
+
+
+def make_hidden(w: Workload, T: Optional[int] = None) -> np.ndarray:
+    """Residual stream h [T, D] ~ N(0, 9) in the activation dtype."""
+    T = w.T if T is None else T
+    return _encode(normal_f32(w.seed, TID_H, 0, (T, w.D), 3.0), w.dtype)
+
+
+def make_dense(w: Workload, F: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(w1 [F, D], w3 [F, D], w2 [D, F]) of a dense SiLU-gated FFN of width F."""
+    s_in, s_out = 1.0 / np.sqrt(w.D), 1.0 / np.sqrt(F)
+    w1 = normal_f32(w.weight_seed, TID_DW1, 0, (F, w.D), s_in)
+    w3 = normal_f32(w.weight_seed, TID_DW3, 0, (F, w.D), s_in)
+    w2 = normal_f32(w.weight_seed, TID_DW2, 0, (w.D, F), s_out)
     return _encode(w1, w.dtype), _encode(w3, w.dtype), _encode(w2, w.dtype)
 
 
