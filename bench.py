@@ -81,24 +81,38 @@ def algorithmic(w, counts):
     return f, b, layer_flops, layer_bytes, n_active
 
 
-def time_layer(glm, torch, dev, w, steps, warmup, ws):
-    out = torch.empty((w.T, w.D), dtype=torch.float32, device="cuda")
-    args = dev.args()
+def time_calls(glm, torch, call, steps, warmup):
+    """Run ``call(trace)`` warmup + steps times; wall time of the timed steps
+    (synchronised on both sides) and the per-call stage times from the HIP
+    events the library records on the call's stream."""
     for _ in range(warmup):
-        glm.forward(*args, w.k, w.scale, out=out, workspace=ws)
+        call(None)
     torch.cuda.synchronize()
     tr = glm.Trace(max_calls=steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        glm.forward(*args, w.k, w.scale, out=out, workspace=ws, trace=tr)
+        call(tr)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     stage_ms, n = tr.read()
     tr.close()
-    per_call = {s: v / n for s, v in stage_ms.items()}
+    return elapsed, {s: v / n for s, v in stage_ms.items()}
+
+
+def time_layer(glm, torch, dev, w, steps, warmup, ws, **opts):
+    out = torch.empty((w.T, w.D), dtype=torch.float32, device="cuda")
+    args = dev.args()
+    scale = opts.pop("scale", w.scale)
+    x = opts.pop("x", args[0])
+    args = (x,) + tuple(args[1:])
+
+    def call(tr):
+        glm.forward(*args, w.k, scale, out=out, workspace=ws, trace=tr, **opts)
+
+    elapsed, per_call = time_calls(glm, torch, call, steps, warmup)
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    glm.forward(*args, w.k, w.scale, out=out, workspace=ws, topk_idx=idx)
+    glm.forward(*args, w.k, scale, out=out, workspace=ws, topk_idx=idx, **opts)
     counts = torch.bincount(idx.flatten().long(), minlength=w.E).cpu().numpy()
     return elapsed, per_call, counts
 
@@ -133,6 +147,40 @@ def record(w, elapsed, steps, per_call, counts, bound, traffic_kind=None):
     return ms, roof, layer, load
 
 
+def dense_record(glm, torch, w, F, dw, steps, warmup, ws, bound):
+    """The dense SiLU-gated FFN (hidden w.D, width F) on the grouped path."""
+    T, D = w.T, w.D
+    import workloads as wl
+    from workloads.device import to_device
+    x = to_device(wl.make_x(w))
+    out = torch.empty((T, D), dtype=torch.float32, device="cuda")
+
+    def call(tr):
+        glm.dense_ffn(x, *dw, out=out, workspace=ws, trace=tr)
+
+    elapsed, pc = time_calls(glm, torch, call, steps, warmup)
+    ms = elapsed * 1e3 / steps
+    f = {"gate_up": 2.0 * T * 2 * F * D, "down": 2.0 * T * D * F}
+    b = {"gate_up": 2 * F * D * 2 + T * D * 2, "down": D * F * 2 + T * F * 2}
+    dom = max(("gate_up", "down"), key=lambda s: pc[s])
+    t = pc[dom] * 1e-3
+    if bound == "mfma":
+        ach = f[dom] / t / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "work_per_launch": f[dom], "avg_launch_ms": round(pc[dom], 4)}
+    else:
+        ach = b[dom] / t / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "work_per_launch": b[dom], "avg_launch_ms": round(pc[dom], 4)}
+    return {"workload": f"dense FFN hidden {D} width {F}, {T} tokens", "tokens": T,
+            "value": round(T * steps / elapsed, 1), "unit": "tokens/s", "steps": steps,
+            "ms_per_step": round(ms, 4), "roofline": roof,
+            "stages_ms": {s: round(v, 4) for s, v in pc.items() if v > 0}}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -165,6 +213,65 @@ def cpu_baseline(w, n_tokens):
                        f"expert; weights drawn before timing")}
 
 
+def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
+    """The layer's options and the dense FFN, at the prefill (and decode) sizes."""
+    from workloads.device import to_device
+    res = {}
+    base = None
+    # pre-norm block: RMSNorm of the residual stream in, residual add out
+    h = to_device(wl.make_hidden(wp))
+    e, pc, c = time_layer(glm, torch, dev, wp, args.steps, args.warmup, ws, x=h,
+                          norm_weight=norm_w, residual=True)
+    nb = wp.T * wp.D * 2 * 2 + wp.D * 4   # read h, write the normalised bf16 input
+    res["prefill_block"] = {
+        "what": "RMSNorm(h) -> layer -> + h", "value": round(wp.T * args.steps / e, 1),
+        "unit": "tokens/s", "ms_per_step": round(e * 1e3 / args.steps, 4),
+        "norm_roofline": {"bound": "hbm", "kernel": "rmsnorm", "work_per_launch": nb,
+                          "avg_launch_ms": round(pc["norm"], 4),
+                          "achieved": round(nb / (pc["norm"] * 1e-3) / 1e9, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(nb / (pc["norm"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
+    log(f"prefill block: {res['prefill_block']['value']:,.0f} tokens/s, stages {pc}")
+    del h
+    # group-limited routing (8 groups of 32, 4 kept) at scale 1.0
+    e, pc, c = time_layer(glm, torch, dev, wp, args.steps, args.warmup, ws, n_group=8,
+                          topk_group=4, group_topk=2, scale=1.0)
+    res["prefill_group_routing"] = {
+        "what": "n_group 8, topk_group 4, group_topk 2, scale 1.0",
+        "value": round(wp.T * args.steps / e, 1), "unit": "tokens/s",
+        "ms_per_step": round(e * 1e3 / args.steps, 4),
+        "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
+    log(f"prefill group routing: {res['prefill_group_routing']['value']:,.0f} tokens/s, "
+        f"stages {pc}")
+    if wd:
+        dd = type(dev)(wd, to_device(wl.make_x(wd)), dev.router_w,
+                       to_device(wl.make_corr_bias(wd)), dev.w1, dev.w3, dev.w2, dev.sw1,
+                       dev.sw3, dev.sw2)
+        e, pc, c = time_layer(glm, torch, dd, wd, args.decode_steps, args.warmup, ws, n_group=8,
+                              topk_group=4, group_topk=2, scale=1.0)
+        res["decode_group_routing"] = {
+            "value": round(wd.T * args.decode_steps / e, 1), "unit": "tokens/s",
+            "ms_per_step": round(e * 1e3 / args.decode_steps, 4),
+            "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
+    # dense FFN of the leading dense layers (width: see workloads.GLM_DENSE_WIDTH)
+    F = wl.GLM_DENSE_WIDTH
+    t0 = time.time()
+    dw = [to_device(a) for a in wl.make_dense(wp, F)]
+    log(f"dense FFN weights ready ({time.time() - t0:.1f}s)")
+    need = glm.dense_workspace_size(wp.T, wp.D, F)
+    dws = ws if need <= ws.numel() else torch.empty(need, dtype=torch.uint8, device="cuda")
+    res["dense_prefill"] = dense_record(glm, torch, wp, F, dw, args.steps, args.warmup, dws,
+                                        "mfma")
+    log(f"dense prefill: {res['dense_prefill']['value']:,.0f} tokens/s")
+    if wd:
+        res["dense_decode"] = dense_record(glm, torch, wd, F, dw, args.decode_steps,
+                                           args.warmup, dws, "hbm")
+        log(f"dense decode: {res['dense_decode']['value']:,.0f} tokens/s")
+    del dw, dws
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +281,8 @@ def main():
     ap.add_argument("--decode-workload", default="glm_decode", help="'' to skip")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=48, help="0 to skip the oracle baseline")
+    ap.add_argument("--no-variants", dest="variants", action="store_false",
+                    help="skip the block / group-routing / dense-FFN measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -200,7 +309,10 @@ def main():
     log(f"weights resident in HBM ({time.time() - t0:.1f}s)")
 
     wd = wl.WORKLOADS[args.decode_workload] if args.decode_workload else None
-    sizes = [glm.workspace_size(wp.T, wp.D, wp.E, wp.F, wp.Fs, wp.k)]
+    norm_w = to_device(wl.make_norm_weight(wp))
+    block_opts = glm.options(norm_weight=norm_w, residual=True, D=wp.D)
+    sizes = [glm.workspace_size(wp.T, wp.D, wp.E, wp.F, wp.Fs, wp.k),
+             glm.workspace_size(wp.T, wp.D, wp.E, wp.F, wp.Fs, wp.k, opts=block_opts)]
     if wd:
         sizes.append(glm.workspace_size(wd.T, wd.D, wd.E, wd.F, wd.Fs, wd.k))
     ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
@@ -238,6 +350,9 @@ def main():
                           "ms_per_step": round(ms2, 4), "roofline": roof2,
                           "layer_roofline": layer2, "routing_load": load2,
                           "stages_ms": {s: round(v, 4) for s, v in pc2.items()}}
+
+    if args.variants:
+        line["variants"] = variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args)
 
     del dev
     torch.cuda.empty_cache()

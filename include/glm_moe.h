@@ -119,14 +119,15 @@ GLM_MOE_API int glm_moe_forward(const glm_moe_dims* d, const void* x, const floa
 
 /* Stages of one forward call, in launch order (used by the stage trace). */
 enum {
-  GLM_MOE_STAGE_ROUTER_LOGITS = 0,
-  GLM_MOE_STAGE_ROUTER_TOPK = 1,
-  GLM_MOE_STAGE_SCAN = 2,
-  GLM_MOE_STAGE_SCATTER = 3,
-  GLM_MOE_STAGE_GATE_UP = 4,
-  GLM_MOE_STAGE_DOWN = 5,
-  GLM_MOE_STAGE_SHARED_COMBINE = 6,
-  GLM_MOE_NUM_STAGES = 7
+  GLM_MOE_STAGE_NORM = 0,          /* pre-norm RMSNorm (empty unless requested) */
+  GLM_MOE_STAGE_ROUTER_LOGITS = 1,
+  GLM_MOE_STAGE_ROUTER_TOPK = 2,
+  GLM_MOE_STAGE_SCAN = 3,
+  GLM_MOE_STAGE_SCATTER = 4,
+  GLM_MOE_STAGE_GATE_UP = 5,
+  GLM_MOE_STAGE_DOWN = 6,
+  GLM_MOE_STAGE_SHARED_COMBINE = 7, /* combine (+ residual add) */
+  GLM_MOE_NUM_STAGES = 8
 };
 
 /* Optional per-stage timing with HIP events recorded on the call's stream.
@@ -204,13 +205,15 @@ GLM_MOE_API int glm_moe_forward_ex(const glm_moe_dims* d, const glm_moe_options*
  * one group.  Uses d->T, d->D, d->F_shared (the dense width) and the dtypes;
  * E and F are ignored.  w1, w3 [F_shared][D]; w2 [D][F_shared]; out [T][D]
  * fp32.  opts may give norm_weight / norm_eps / add_residual (grouping
- * fields are ignored).  Workspace from glm_moe_dense_workspace_size. */
+ * fields are ignored).  Workspace from glm_moe_dense_workspace_size.
+ * `trace` (nullable) records the stages as for glm_moe_forward_traced; the
+ * router and scatter stages are empty. */
 GLM_MOE_API int glm_moe_dense_workspace_size(const glm_moe_dims* d, const glm_moe_options* opts,
                                              size_t* bytes);
 GLM_MOE_API int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* opts,
                                   const void* x, const void* w1, const void* w3, const void* w2,
                                   float* out, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream);
+                                  hipStream_t stream, glm_moe_trace* trace);
 
 /* Static text for a status code. */
 GLM_MOE_API const char* glm_moe_status_string(int status);

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libglm_moe.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
-STAGES = ("router_logits", "router_topk", "scan", "scatter", "gate_up", "down",
+STAGES = ("norm", "router_logits", "router_topk", "scan", "scatter", "gate_up", "down",
           "shared_combine")
 
 
@@ -65,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.glm_moe_forward_ex.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
                                          vp, vp, vp, sz, vp, vp]
         L.glm_moe_dense_workspace_size.argtypes = [pd, po, ctypes.POINTER(sz)]
-        L.glm_moe_dense_ffn.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.glm_moe_dense_ffn.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.glm_moe_trace_create.argtypes = [ctypes.POINTER(vp), i32]
         L.glm_moe_trace_destroy.argtypes = [vp]
         L.glm_moe_trace_reset.argtypes = [vp]
@@ -261,7 +261,7 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
 def dense_ffn(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, *,
               norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
-              residual: bool = False) -> torch.Tensor:
+              residual: bool = False, trace: Optional[Trace] = None) -> torch.Tensor:
     """A dense SiLU-gated FFN on the same kernels; returns ``out`` [T, D] float32."""
     T, D = x.shape
     F = w1.shape[0]
@@ -277,6 +277,7 @@ def dense_ffn(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
         ctypes.byref(d), ctypes.byref(o), _ptr(x, "x", dt, (T, D)),
         _ptr(w1, "w1", dt, (F, D)), _ptr(w3, "w3", dt, (F, D)), _ptr(w2, "w2", dt, (D, F)),
         _ptr(out, "out", torch.float32, (T, D)),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(),
+        None if trace is None else trace.handle)
     _check(st, "glm_moe_dense_ffn")
     return out

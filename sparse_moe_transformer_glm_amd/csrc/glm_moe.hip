@@ -222,7 +222,7 @@ struct Recorder {
   } while (0)
 
 // RMSNorm of the residual stream into the workspace when requested; returns
-// the input the layer runs on.  (Timed as part of the router-logits stage.)
+// the input the layer runs on.
 int layer_input(const Plan& P, const void* x, void* ws, hipStream_t s, const void** xin) {
   *xin = x;
   if (P.norm_weight) {
@@ -405,9 +405,10 @@ int glm_moe_forward_ex(const glm_moe_dims* d, const glm_moe_options* opts, const
   Recorder rec(trace, s);
   int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, P.idx);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, P.w);
-  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_NORM));
   const void* xin;
   if ((st = layer_input(P, x, ws, s, &xin))) return st;
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
   if ((st = run_router(P, xin, router_w, ws, s))) return st;
   GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
   if ((st = run_topk(P, corr_bias, scale, idx, wts, ws, s))) return st;
@@ -449,7 +450,8 @@ int glm_moe_dense_workspace_size(const glm_moe_dims* d, const glm_moe_options* o
 
 int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* opts, const void* x,
                       const void* w1, const void* w3, const void* w2, float* out,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      glm_moe_trace* trace) {
   Plan P;
   int st = make_plan(d, 0, opts, true, &P);
   if (st) return st;
@@ -458,9 +460,12 @@ int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* opts, const 
       (st = check_ptr(w2, "w2")) || (st = check_ptr(out, "out")))
     return st;
   if ((st = check_ws(P, workspace, workspace_bytes))) return st;
-  Recorder rec(nullptr, stream);
+  Recorder rec(trace, stream);
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_NORM));
   const void* xin;
   if ((st = layer_input(P, x, workspace, stream, &xin))) return st;
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
   return run_experts(P, x, xin, nullptr, nullptr, nullptr, nullptr, nullptr, w1, w3, w2, out,
                      workspace, stream, rec);
 }

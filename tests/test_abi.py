@@ -284,10 +284,13 @@ def test_dense_argument_checks():
     for i in range(5):
         p = list(good)
         p[i] = 0
-        assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *p, FAKE, need, None) == glm.EINVAL
+        assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *p, FAKE, need, None,
+                                   None) == glm.EINVAL
         p[i] = FAKE + 2
-        assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *p, FAKE, need, None) == glm.EINVAL
-    assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *good, FAKE, need - 1,
+        assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *p, FAKE, need, None,
+                                   None) == glm.EINVAL
+    assert L.glm_moe_dense_ffn(ctypes.byref(d), None, *good, FAKE, need - 1, None,
                                None) == glm.EWORKSPACE
     d0 = Dims(0, 128, 0, 0, 64, glm.BF16, glm.BF16)
-    assert L.glm_moe_dense_ffn(ctypes.byref(d0), None, 0, 0, 0, 0, 0, 0, 0, None) == glm.OK
+    assert L.glm_moe_dense_ffn(ctypes.byref(d0), None, 0, 0, 0, 0, 0, 0, 0, None,
+                               None) == glm.OK
