@@ -59,10 +59,9 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int ST_, int MB_, int PP_ = 0>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int ST_, int MB_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, ST = ST_, MB = MB_;
-  static constexpr bool PP = PP_ != 0;        // ping-pong schedule (two wave groups)
   static constexpr int NW = WM * WN, NT = NW * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / MB, FN = TN / MB;
@@ -277,94 +276,6 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       if constexpr (ST > 3) if (kt + 3 < nk) step(std::integral_constant<int, 3 % ST>{}, kt + 3);
     }
   };
-  // Ping-pong schedule.  The two wave rows form two groups; SIMD i runs wave
-  // i of each.  Every k-step is a memory phase (read the k-step's fragments
-  // from LDS, issue this wave's share of the DMA ST-1 steps ahead, wait for
-  // the next stage) and a compute phase (the MFMAs on those fragments), each
-  // closed by a workgroup barrier.  Group 1 starts one phase late, so on each
-  // SIMD one wave issues MFMAs while the other moves data.
-  auto run_pp = [&](auto live_c) {
-    constexpr int LIVE = decltype(live_c)::value;
-    constexpr int KS = C::KSUB;
-    bf16x8 fa[KS][FM > 0 ? FM : 1], fb[KS][FN];
-    const int grp = wm;  // 0 or 1
-    auto read_all = [&](const bf16_t* st) {
-      if constexpr (LIVE > 0) {
-#pragma unroll
-        for (int sub = 0; sub < KS; ++sub) {
-          const int kc = (MB == 32 ? 2 * sub : 4 * sub) + lk;
-          const int off = (kc ^ sw) * 8;
-          const bf16_t* sa = st + (wrow0 + lr) * BK + off;
-          const bf16_t* sb = st + (BM + wn * TN + lr) * BK + off;
-#pragma unroll
-          for (int n = 0; n < FN; ++n)
-            fb[sub][n] = *reinterpret_cast<const bf16x8*>(sb + n * MB * BK);
-#pragma unroll
-          for (int m = 0; m < LIVE; ++m)
-            fa[sub][m] = *reinterpret_cast<const bf16x8*>(sa + m * MB * BK);
-        }
-      }
-    };
-    auto mma_all = [&]() {
-#pragma unroll
-      for (int sub = 0; sub < KS; ++sub)
-#pragma unroll
-        for (int m = 0; m < LIVE; ++m)
-#pragma unroll
-          for (int n = 0; n < FN; ++n) {
-            if constexpr (MB == 32)
-              acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub][m], fb[sub][n],
-                                                                  acc[m][n], 0, 0, 0);
-            else
-              acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[sub][m], fb[sub][n],
-                                                                  acc[m][n], 0, 0, 0);
-          }
-    };
-    // wait until this wave's DMA of stage `need` has landed; the stages it
-    // issued after that one may stay in flight
-    auto wait_stage = [&](int need, int issued_last) {
-      const int after = min(issued_last, nk - 1) - need;
-      if (after >= 2) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * 2));
-      else if (after == 1) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW));
-      else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
-    };
-    static_assert(ST >= 2 && ST <= 4, "ping-pong ring of 2..4 stages");
-#pragma unroll
-    for (int s = 0; s < ST - 1; ++s)
-      if (s < nk) issue(stage_ptr(s), s);
-    wait_stage(0, ST - 2);
-    lds_barrier();
-    if (grp == 1) lds_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
-      // memory phase
-      read_all(stage_ptr(kt % ST));
-      if (kt + ST - 1 < nk) issue(stage_ptr((kt + ST - 1) % ST), kt + ST - 1);
-      if (grp == 1 && kt + 1 < nk) wait_stage(kt + 1, kt + ST - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // compute phase
-      __builtin_amdgcn_s_setprio(1);
-      mma_all();
-      __builtin_amdgcn_s_setprio(0);
-      if (grp == 0 && kt + 1 < nk) wait_stage(kt + 1, kt + ST - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (grp == 0) lds_barrier();
-  };
-
-  if constexpr (C::PP) {
-    static_assert(C::WM == 2 && C::WN * 2 == NW, "two wave groups of one wave row each");
-    switch (live_m) {
-      case 1: run_pp(std::integral_constant<int, 1>{}); break;
-      case 2: if constexpr (FM >= 2) run_pp(std::integral_constant<int, 2>{}); break;
-      case 3: if constexpr (FM >= 3) run_pp(std::integral_constant<int, 3>{}); break;
-      case 4: if constexpr (FM >= 4) run_pp(std::integral_constant<int, 4>{}); break;
-      default: run_pp(std::integral_constant<int, 0>{}); break;
-    }
-  } else {
   static_assert(C::KSUB % 2 == 0, "fragment slots alternate per sub-step");
   static_assert(FM <= 4, "live-block dispatch covers up to 4 row blocks");
   switch (live_m) {
@@ -384,8 +295,6 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
         if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST);
       }
     }
-  }
-
   }
 
   // ------------------------------------------------------------ epilogue
