@@ -33,6 +33,8 @@ from typing import Callable, Optional, Sequence, Tuple
 
 import numpy as np
 
+from . import mx
+
 Expert = Tuple[np.ndarray, np.ndarray, np.ndarray]
 
 
@@ -237,3 +239,51 @@ def block_ffn(h, norm_weight, eps: float, x_dtype: str, layer) -> Tuple[np.ndarr
 def dense_ffn(x, w1, w3, w2) -> np.ndarray:
     """A dense SiLU-gated MLP (the leading dense layers use this form)."""
     return expert_mlp(decode(x), w1, w3, w2)
+
+
+# ------------------------------------------------------ MXFP8 expert variant
+
+MxTensor = Tuple[np.ndarray, np.ndarray]        # (E4M3 codes, E8M0 scales)
+MxExpert = Tuple[MxTensor, MxTensor, MxTensor]  # w1, w3, w2
+
+
+def expert_mlp_mx(xq: np.ndarray, w1: MxTensor, w3: MxTensor, w2: MxTensor) -> np.ndarray:
+    """The SiLU-gated expert MLP with MXFP8 weights, on an MXFP8 input.
+
+    ``xq`` holds the values of the already quantised input rows.  The gated
+    hidden value SiLU(x w1^T) * (x w3^T) is quantised to MXFP8 along the hidden
+    dimension before the w2 product, as the down projection consumes it in that
+    format.
+    """
+    W1, W3, W2 = mx.dequantize(*w1), mx.dequantize(*w3), mx.dequantize(*w2)
+    h = silu(xq @ W1.T) * (xq @ W3.T)
+    return mx.fake_quantize(h) @ W2.T
+
+
+def forward_mx(x, router_w, corr_bias,
+               experts: Callable[[int], MxExpert],
+               shared: MxExpert,
+               top_k: int, scale: float,
+               force_idx: Optional[np.ndarray] = None,
+               routing: Optional[Routing] = None,
+               n_group: int = 1, topk_group: int = 1,
+               group_topk: int = 2) -> Tuple[np.ndarray, Routing]:
+    """The layer with MXFP8 expert weights (``oracle.mx``): ``(out, routing)``.
+
+    Routing (steps 1-4) runs on the input as given, exactly as in ``forward``.
+    The expert products take the input quantised to MXFP8 per token along the
+    hidden dimension (blocks of 32), and the gated hidden values quantised the
+    same way along the expert width; everything else is ``forward``.
+    """
+    xd = decode(x)
+    r = routing if routing is not None else route(xd, router_w, corr_bias, top_k, scale, force_idx,
+                                                  n_group, topk_group, group_topk)
+    xq = mx.fake_quantize(xd)
+    T, D = xd.shape
+    routed = np.zeros((T, D))
+    for e in np.unique(r.idx):
+        tok, slot = np.nonzero(r.idx == e)
+        y = expert_mlp_mx(xq[tok], *experts(int(e)))
+        routed[tok] += r.weight[tok, slot][:, None] * y
+    out = routed + expert_mlp_mx(xq, *shared)
+    return out, r

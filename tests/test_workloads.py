@@ -55,3 +55,28 @@ def test_iter_experts_order_and_window():
     assert es == list(range(w.E))
     L = wl.make_layer(w, threads=2)
     np.testing.assert_array_equal(L.w2[5], wl.make_expert(w, 5)[2])
+
+
+def test_mxfp8_encoder_agrees_with_the_oracle_format():
+    """The generator's MXFP8 encoder (integer rounding of fp32 bit patterns)
+    and the oracle's (float64 frexp/round) are separate code for one format."""
+    import oracle
+    rng = np.random.default_rng(7)
+    a = (rng.standard_normal((40, 256)) * np.exp2(rng.integers(-12, 8, (40, 1)))).astype(np.float32)
+    a[5, 32:64] = 0
+    a[6, :32] = np.float32(448.0) * np.float32(2.0 ** -3)   # block max exactly at a boundary
+    c1, s1 = wl.f32_to_mxfp8(a)
+    c2, s2 = oracle.mx.quantize(a.astype(np.float64))
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c1, c2)
+
+
+def test_mxfp8_layer_shapes():
+    w = wl.WORKLOADS["mid_mx"].with_(T=8, E=4)
+    L = wl.make_layer(w, threads=2)
+    assert L.w1.dtype == np.uint8 and L.w1.shape == (4, w.F, w.D)
+    assert L.w1s.shape == (4, w.F, w.D // 32) and L.w2s.shape == (4, w.D, w.F // 32)
+    assert L.sw2s.shape == (w.D, w.Fs // 32)
+    assert L.x.dtype == np.uint16
+    (c, s), _, _ = L.expert(1)
+    assert c.shape == (w.F, w.D) and s.shape == (w.F, w.D // 32)

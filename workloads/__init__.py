@@ -52,7 +52,8 @@ class Workload:
     k: int
     F: int
     Fs: int
-    dtype: str  # "f32" or "bf16": activations and expert weights
+    dtype: str  # "f32", "bf16" (activations and weights), "mxfp8" (bf16 activations,
+                #  MXFP8 expert weights)
     scale: float
     bias_std: float
     seed: int
@@ -78,6 +79,9 @@ WORKLOADS = {
     # mid-size bf16 layer
     "mid_bf16": Workload("mid_bf16", T=512, D=1024, E=64, k=4, F=512, Fs=512, dtype="bf16",
                          scale=2.5, bias_std=0.1, seed=2, weight_seed=2),
+    # mid-size layer with MXFP8 expert weights (bf16 activations)
+    "mid_mx": Workload("mid_mx", T=512, D=1024, E=64, k=4, F=512, Fs=512, dtype="mxfp8",
+                       scale=2.5, bias_std=0.1, seed=2, weight_seed=2),
     # GLM-5.2 shape, 64-token decode step
     "glm_decode": Workload("glm_decode", T=64, D=6144, E=256, k=8, F=2048, Fs=2048, dtype="bf16",
                            scale=2.5, bias_std=0.1, seed=3, weight_seed=GLM_WEIGHT_SEED),
@@ -93,6 +97,14 @@ WORKLOADS = {
     "glm_skew_mild": Workload("glm_skew_mild", T=4096, D=6144, E=256, k=8, F=2048, Fs=2048,
                               dtype="bf16", scale=2.5, bias_std=0.05, seed=55,
                               weight_seed=GLM_WEIGHT_SEED, hot_count=16, hot_value=0.2),
+    # the GLM-5.2 decode and prefill batches with MXFP8 expert weights (the same
+    # fp32 draws, encoded as MXFP8 instead of bf16)
+    "glm_decode_mx": Workload("glm_decode_mx", T=64, D=6144, E=256, k=8, F=2048, Fs=2048,
+                              dtype="mxfp8", scale=2.5, bias_std=0.1, seed=3,
+                              weight_seed=GLM_WEIGHT_SEED),
+    "glm_prefill_mx": Workload("glm_prefill_mx", T=8192, D=6144, E=256, k=8, F=2048, Fs=2048,
+                               dtype="mxfp8", scale=2.5, bias_std=0.01, seed=4,
+                               weight_seed=GLM_WEIGHT_SEED),
 }
 
 
@@ -122,8 +134,40 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return b.astype(np.uint16)
 
 
+def f32_to_mxfp8(a: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Encode fp32 values as OCP MXFP8 along the last axis (blocks of 32).
+
+    Returns (E4M3 codes uint8, E8M0 scales uint8 [..., n/32]).  Block scale:
+    the smallest 2^s with max|v| <= 448 * 2^s; elements v * 2^-s rounded to the
+    nearest E4M3 value, ties to even (integer rounding of the fp32 bit pattern
+    for normal results, of v * 2^9 for results below 2^-6).
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    n = a.shape[-1]
+    assert n % 32 == 0, "MXFP8 rows must be a multiple of 32 long"
+    blk = a.reshape(a.shape[:-1] + (n // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    mant, ex = np.frexp(amax)                          # amax = mant * 2^ex
+    s = np.where(mant <= np.float32(0.875), ex - 9, ex - 8)
+    s = np.where(amax == 0, 0, s).astype(np.int32)
+    y = np.ldexp(blk, -s[..., None]).astype(np.float32)  # exact power-of-two scaling
+    mag = np.abs(y)
+    u = mag.view(np.uint32).astype(np.int64)
+    normal = (u >> 23) >= (127 - 6)
+    rn = (u + 0x7FFFF + ((u >> 20) & 1)) >> 20         # 8-bit exponent, 3-bit mantissa
+    code = np.where(normal, rn - ((127 - 7) << 3), np.rint(mag * np.float32(512.0)))
+    code = code.astype(np.int64) | np.where(np.signbit(y) & (mag > 0), 0x80, 0)
+    return code.astype(np.uint8).reshape(a.shape), (s + 127).astype(np.uint8)
+
+
 def _encode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Activations (and f32/bf16 weights) in the workload's storage format."""
     return a if dtype == "f32" else f32_to_bf16_bits(a)
+
+
+def _encode_weight(a: np.ndarray, dtype: str):
+    """Expert weights: as ``_encode``, or an (codes, scales) pair for MXFP8."""
+    return f32_to_mxfp8(a) if dtype == "mxfp8" else _encode(a, dtype)
 
 
 # ---------------------------------------------------------------- per tensor
@@ -152,7 +196,7 @@ def make_expert(w: Workload, e: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray
     w1 = normal_f32(w.weight_seed, TID_W1, e, (w.F, w.D), s_in)
     w3 = normal_f32(w.weight_seed, TID_W3, e, (w.F, w.D), s_in)
     w2 = normal_f32(w.weight_seed, TID_W2, e, (w.D, w.F), s_out)
-    return _encode(w1, w.dtype), _encode(w3, w.dtype), _encode(w2, w.dtype)
+    return _encode_weight(w1, w.dtype), _encode_weight(w3, w.dtype), _encode_weight(w2, w.dtype)
 
 
 def make_shared(w: Workload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -161,7 +205,7 @@ def make_shared(w: Workload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     w1 = normal_f32(w.weight_seed, TID_SW1, 0, (w.Fs, w.D), s_in)
     w3 = normal_f32(w.weight_seed, TID_SW3, 0, (w.Fs, w.D), s_in)
     w2 = normal_f32(w.weight_seed, TID_SW2, 0, (w.D, w.Fs), s_out)
-    return _encode(w1, w.dtype), _encode(w3, w.dtype), _encode(w2, w.dtype)
+    return _encode_weight(w1, w.dtype), _encode_weight(w3, w.dtype), _encode_weight(w2, w.dtype)
 
 
 def make_norm_weight(w: Workload) -> np.ndarray:
@@ -227,10 +271,42 @@ class HostLayer:
     sw1: np.ndarray
     sw3: np.ndarray
     sw2: np.ndarray
+    # MXFP8 weights: the fields above hold E4M3 codes, these the E8M0 scales
+    # (one per 32 elements along each row)
+    w1s: Optional[np.ndarray] = None  # [E, F, D/32]
+    w3s: Optional[np.ndarray] = None
+    w2s: Optional[np.ndarray] = None  # [E, D, F/32]
+    sw1s: Optional[np.ndarray] = None
+    sw3s: Optional[np.ndarray] = None
+    sw2s: Optional[np.ndarray] = None
+
+    def expert(self, e: int):
+        """Expert e's weights: (w1, w3, w2), or ((codes, scales) x 3) for MXFP8."""
+        if self.w1s is None:
+            return self.w1[e], self.w3[e], self.w2[e]
+        return ((self.w1[e], self.w1s[e]), (self.w3[e], self.w3s[e]), (self.w2[e], self.w2s[e]))
+
+    def shared(self):
+        if self.sw1s is None:
+            return self.sw1, self.sw3, self.sw2
+        return ((self.sw1, self.sw1s), (self.sw3, self.sw3s), (self.sw2, self.sw2s))
 
 
 def make_layer(w: Workload, threads: Optional[int] = None) -> HostLayer:
     """Whole layer on the host (use for sizes that fit comfortably in RAM)."""
+    x, rw, cb = make_x(w), make_router_w(w), make_corr_bias(w)
+    if w.dtype == "mxfp8":
+        w1 = np.empty((w.E, w.F, w.D), np.uint8)
+        w3 = np.empty((w.E, w.F, w.D), np.uint8)
+        w2 = np.empty((w.E, w.D, w.F), np.uint8)
+        w1s = np.empty((w.E, w.F, w.D // 32), np.uint8)
+        w3s = np.empty((w.E, w.F, w.D // 32), np.uint8)
+        w2s = np.empty((w.E, w.D, w.F // 32), np.uint8)
+        for e, (a, b, c) in iter_experts(w, threads):
+            (w1[e], w1s[e]), (w3[e], w3s[e]), (w2[e], w2s[e]) = a, b, c
+        (sw1, sw1s), (sw3, sw3s), (sw2, sw2s) = make_shared(w)
+        return HostLayer(w, x, rw, cb, w1, w3, w2, sw1, sw3, sw2, w1s, w3s, w2s, sw1s, sw3s,
+                         sw2s)
     et = np.float32 if w.dtype == "f32" else np.uint16
     w1 = np.empty((w.E, w.F, w.D), et)
     w3 = np.empty((w.E, w.F, w.D), et)
@@ -238,4 +314,4 @@ def make_layer(w: Workload, threads: Optional[int] = None) -> HostLayer:
     for e, (a, b, c) in iter_experts(w, threads):
         w1[e], w3[e], w2[e] = a, b, c
     sw1, sw3, sw2 = make_shared(w)
-    return HostLayer(w, make_x(w), make_router_w(w), make_corr_bias(w), w1, w3, w2, sw1, sw3, sw2)
+    return HostLayer(w, x, rw, cb, w1, w3, w2, sw1, sw3, sw2)
