@@ -56,13 +56,15 @@ typedef enum {
 
 typedef enum {
   GLM_MOE_F32 = 0,
-  GLM_MOE_BF16 = 1
+  GLM_MOE_BF16 = 1,
+  GLM_MOE_MXFP8 = 2  /* weights only: OCP MX FP8, see glm_moe_forward_mx */
 } glm_moe_dtype;
 
 /* Layer sizes.  T tokens, hidden D, E routed experts, routed expert width F,
  * shared expert width F_shared.  act_dtype is the dtype of x; weight_dtype is
  * the dtype of w1/w3/w2 and the shared expert.  Supported pairs: F32/F32 and
- * BF16/BF16.  router_w, corr_bias, out and topk_w are always fp32. */
+ * BF16/BF16 (glm_moe_forward*), BF16/MXFP8 (glm_moe_forward_mx).  router_w,
+ * corr_bias, out and topk_w are always fp32. */
 typedef struct {
   int32_t T, D, E, F, F_shared;
   int32_t act_dtype;
@@ -214,6 +216,44 @@ GLM_MOE_API int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* 
                                   const void* x, const void* w1, const void* w3, const void* w2,
                                   float* out, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream, glm_moe_trace* trace);
+
+/* MXFP8 expert weights (OCP Microscaling v1.0 MXFP8): each tensor is E4M3
+ * codes (1 byte; bias 7, max 448, no infinities) in the bf16 layout above, plus
+ * one E8M0 scale byte (value 2^(s - 127)) per 32 consecutive elements along
+ * its rows (the contraction dimension):
+ *   w1, w3 [E][F][D] codes, w1_scale, w3_scale [E][F][D/32];
+ *   w2 [E][D][F] codes, w2_scale [E][D][F/32];
+ *   shared_w1, shared_w3 [F_shared][D], scales [F_shared][D/32];
+ *   shared_w2 [D][F_shared], scale [D][F_shared/32].
+ * The pages name FP8 GLM-5.2 artifacts (frontier-model-atlas "GLM-5.2 model
+ * anatomy", release panel) without their scaling; this block format is the
+ * one gfx950 applies inside its FP8 MFMA. */
+typedef struct {
+  const void* w1; const void* w1_scale;
+  const void* w3; const void* w3_scale;
+  const void* w2; const void* w2_scale;
+  const void* shared_w1; const void* shared_w1_scale;
+  const void* shared_w3; const void* shared_w3_scale;
+  const void* shared_w2; const void* shared_w2_scale;
+} glm_moe_mx_weights;
+
+/* The layer with MXFP8 expert weights.  d->act_dtype must be GLM_MOE_BF16 and
+ * d->weight_dtype GLM_MOE_MXFP8; D, F and F_shared must be multiples of 128
+ * (else EUNSUPPORTED).  Routing is that of glm_moe_forward on the bf16 input.
+ * The expert products take the input quantised to MXFP8 per token (blocks of
+ * 32 along D) and the gated hidden values quantised per row (blocks of 32
+ * along F): block scale = the smallest power of two keeping every element
+ * within +-448, elements rounded to nearest E4M3, ties to even.  Accumulation
+ * is fp32; the routed weights, shared expert and combine are as in
+ * glm_moe_forward.  Workspace from glm_moe_workspace_size_ex with the same
+ * dims.  Every pointer of `w` must be non-null and 16-byte aligned.  Other
+ * arguments, options and errors as glm_moe_forward_ex. */
+GLM_MOE_API int glm_moe_forward_mx(const glm_moe_dims* d, const glm_moe_options* opts,
+                                   const void* x, const float* router_w, const float* corr_bias,
+                                   const glm_moe_mx_weights* w, int top_k, float scale,
+                                   float* out, int32_t* topk_idx_out, float* topk_w_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   glm_moe_trace* trace);
 
 /* Static text for a status code. */
 GLM_MOE_API const char* glm_moe_status_string(int status);

@@ -20,7 +20,7 @@ from typing import List, Optional
 
 import numpy as np
 
-from . import moe
+from . import moe, mx
 
 
 @dataclasses.dataclass
@@ -133,3 +133,143 @@ BF16_MAX_REL = 2e-2
 BF16_MEAN_REL = 2e-3
 F32_MAX_REL = 1e-5
 WEIGHT_TOL = 1e-5
+# MXFP8 layer against oracle.forward_mx, which performs the same quantisations:
+# differences come from the accumulation precision of the FP8 MFMA and from
+# the hidden values it moves across an E4M3 rounding decision (see mx_explain).
+MX_MEAN_REL = 2e-3   # mean |diff| / rms over all outputs, before explanation
+# explained flips per hidden value, at most: the MFMA's accumulation error
+# (typically 2^-19, at most about 2^-14 of the term sum) moves 0.1-0.4% of the
+# E4M3 decisions of the hidden values on the test layers (GLM shape included)
+MX_FLIP_FRAC = 1e-2
+
+
+# ------------------------------------------------------ MXFP8 rounding ties
+
+# Error budget of an MXFP8 dot product computed by the block-scaled FP8 MFMA,
+# relative to the sum of the magnitudes of its terms.  The MFMA sums each
+# 64-element step with limited internal precision: on gfx950 the error of one
+# step reached 1.7e-5 of that sum, and 6.1e-5 over a 512-long product, for
+# identical inputs; 2^-13 (1.2e-4) is the budget used here.
+MX_HW_REL = 2.0 ** -13
+
+
+def _e4m3_neighbours(a: np.ndarray):
+    """The E4M3 grid values below and above |a| (a in [0, 448])."""
+    _, x = np.frexp(np.maximum(a, 2.0 ** -6))
+    step = np.ldexp(1.0, x - 1 - 3)          # spacing in a's binade (2^-9 below 2^-6)
+    lo = np.floor(a / step) * step
+    return lo, lo + step
+
+
+@dataclasses.dataclass
+class MxFlipReport:
+    rms: float
+    mean_rel: float        # mean |out - ref| / rms before any explanation
+    candidates: int        # hidden values (or blocks) whose rounding is ambiguous
+    flips: int             # candidates taken to explain the difference
+    max_resid_rel: float   # max |residual| / rms after the flips
+    violations: int        # outputs with |residual| > accumulation tolerance
+
+
+def mx_explain(out, ref, x_in, routing: moe.Routing, experts, shared,
+               eps: float = MX_HW_REL, progress=None) -> MxFlipReport:
+    """Explain the difference between an MXFP8 layer output and
+    ``oracle.forward_mx`` by alternative roundings that are equally correct.
+
+    For every expert row the oracle recomputes g = xq W1^T, u = xq W3^T and
+    h = SiLU(g) u, with error budgets eg = eps |xq||W1|^T (likewise eu) and
+    eh = |SiLU'(g) u| eg + |SiLU(g)| eu.  A hidden value whose E4M3 rounding
+    decision lies within eh of its midpoint may take the other neighbour; a
+    block whose maximum lies within its budget of a scale boundary may take
+    the neighbouring scale.  Each such alternative is a candidate whose effect
+    on the token's output row is v = w (alternative - chosen) W2^T (w: the
+    routing weight, 1 for the shared expert).  A candidate is taken when it
+    reduces the squared difference: candidates with 2 <r, v> > |v|^2 against
+    the token's difference r are kept, then taken greedily (largest reduction
+    first, r updated) while any reduces |r|^2.  What remains must lie within the
+    accumulation tolerance eps * w |hq||W2|^T (summed over the token's experts)
+    + 1e-6 * rms, element by element.
+    """
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    xq = mx.fake_quantize(moe.decode(x_in))
+    T, D = xq.shape
+    resid = out - ref
+    tol = np.zeros((T, D))
+    vecs = [[] for _ in range(T)]   # effects of the candidates each token might take
+    count = {"cand": 0, "flips": 0}
+
+    def slot(tok, wt, w1, w3, w2):
+        rows = xq[tok]
+        W1, W3, W2 = mx.dequantize(*w1), mx.dequantize(*w3), mx.dequantize(*w2)
+        g, u = rows @ W1.T, rows @ W3.T
+        ar = np.abs(rows)
+        eg, eu = eps * (ar @ np.abs(W1).T), eps * (ar @ np.abs(W3).T)
+        sg = 1.0 / (1.0 + np.exp(-g))
+        h = g * sg * u
+        eh = (np.abs(sg * (1.0 + g * (1.0 - sg)) * u) * eg + np.abs(g * sg) * eu
+              + 2.0 ** -20 * np.abs(h))
+        hq = mx.fake_quantize(h)
+        tol[tok] += np.abs(wt)[:, None] * eps * (np.abs(hq) @ np.abs(W2).T)
+        n, F = h.shape
+        nb = F // mx.BLOCK
+        hb, eb, qb = (a.reshape(n, nb, mx.BLOCK) for a in (h, eh, hq))
+        amax = np.abs(hb).max(axis=-1)
+        emax = np.take_along_axis(eb, np.abs(hb).argmax(axis=-1)[..., None], axis=-1)[..., 0]
+        s = mx.block_exponent(amax)
+        sc = np.ldexp(1.0, s)[..., None]
+        y, ey = np.abs(hb) / sc, eb / sc
+        lo, hi = _e4m3_neighbours(y)
+        alt = np.where(np.abs(qb) / sc == lo, hi, lo)
+        elem = (np.abs(y - (lo + hi) / 2) <= ey) & (hi <= mx.E4M3_MAX)
+        dv = (wt[:, None, None] * np.where(elem, np.sign(hb) * (alt * sc - np.abs(qb)), 0.0)
+              ).reshape(n, F)
+        R = resid[tok]
+        G = R @ W2                                   # <r_t, W2[:, f]>
+        cn = np.einsum("df,df->f", W2, W2)           # |W2[:, f]|^2
+        pre = elem.reshape(n, F) & (2 * dv * G > dv * dv * cn[None, :])
+        for i, f in zip(*np.nonzero(pre)):
+            vecs[tok[i]].append(dv[i, f] * W2[:, f])
+        count["cand"] += int(elem.sum())
+        # scale candidates: the whole block at the neighbouring scale
+        for s_alt in (-1, 1):
+            near = mx.block_exponent(np.maximum(amax + s_alt * emax, 0.0)) != s
+            for i, b in zip(*np.nonzero(near)):
+                blk = hb[i, b]
+                sa = s[i, b] + s_alt
+                yy = np.minimum(np.abs(blk) / 2.0 ** sa, mx.E4M3_MAX)
+                alt_blk = np.sign(blk) * mx.decode_e4m3(mx.encode_e4m3(yy)) * 2.0 ** sa
+                v = wt[i] * (W2[:, b * mx.BLOCK:(b + 1) * mx.BLOCK] @ (alt_blk - qb[i, b]))
+                count["cand"] += 1
+                if 2 * (R[i] @ v) > v @ v:
+                    vecs[tok[i]].append(v)
+
+    used_experts = np.unique(routing.idx)
+    for n_done, e in enumerate(used_experts):
+        tok, sl = np.nonzero(routing.idx == e)
+        slot(tok, routing.weight[tok, sl], *experts(int(e)))
+        if progress is not None and n_done % 32 == 31:
+            progress(f"mx_explain: {n_done + 1}/{len(used_experts)} experts")
+    slot(np.arange(T), np.ones(T), *shared)
+
+    rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+    left = resid.copy()
+    for t in range(T):
+        if not vecs[t]:
+            continue
+        V = np.array(vecs[t])
+        vv = np.einsum("ij,ij->i", V, V)
+        used = np.zeros(len(V), bool)
+        r = left[t]
+        while True:  # greedy: the candidate that reduces |r|^2 most, until none does
+            gain = 2 * (V @ r) - vv
+            gain[used] = -np.inf
+            c = int(np.argmax(gain))
+            if gain[c] <= 0:
+                break
+            r -= V[c]
+            used[c] = True
+            count["flips"] += 1
+    viol = int((np.abs(left) > tol + 1e-6 * rms).sum())
+    return MxFlipReport(rms, float(np.abs(resid).mean() / rms), count["cand"], count["flips"],
+                        float(np.abs(left).max() / rms), viol)

@@ -4,10 +4,11 @@ The layer runs in hand-written HIP kernels behind the C ABI of
 ``include/glm_moe.h`` (``libglm_moe.so``); this package is its thin Python
 binding.  Build the library with ``python -m sparse_moe_transformer_glm_amd.build``.
 """
-from ._lib import (BF16, EHIP, EINVAL, EUNSUPPORTED, EWORKSPACE, F32, LIB_PATH, OK, STAGES,
-                   GlmMoeError, Options, Trace, dense_ffn, dense_workspace_size, forward, lib,
-                   new_workspace, options, route, workspace_size)
+from ._lib import (BF16, EHIP, EINVAL, EUNSUPPORTED, EWORKSPACE, F32, LIB_PATH, MXFP8, OK,
+                   STAGES, GlmMoeError, MxWeights, Options, Trace, dense_ffn, dense_workspace_size,
+                   forward, forward_mx, lib, new_workspace, options, route, workspace_size)
 
-__all__ = ["BF16", "EHIP", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "F32", "LIB_PATH", "OK",
-           "STAGES", "GlmMoeError", "Options", "Trace", "dense_ffn", "dense_workspace_size",
-           "forward", "lib", "new_workspace", "options", "route", "workspace_size"]
+__all__ = ["BF16", "EHIP", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "F32", "LIB_PATH", "MXFP8",
+           "OK", "STAGES", "GlmMoeError", "MxWeights", "Options", "Trace", "dense_ffn",
+           "dense_workspace_size", "forward", "forward_mx", "lib", "new_workspace", "options",
+           "route", "workspace_size"]

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libglm_moe.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
-F32, BF16 = 0, 1
+F32, BF16, MXFP8 = 0, 1, 2
 STAGES = ("norm", "router_logits", "router_topk", "scan", "scatter", "gate_up", "down",
           "shared_combine")
 
@@ -39,6 +39,13 @@ class Options(ctypes.Structure):
     _fields_ = [("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("group_topk", ctypes.c_int32), ("norm_weight", ctypes.c_void_p),
                 ("norm_eps", ctypes.c_float), ("add_residual", ctypes.c_int32)]
+
+
+class MxWeights(ctypes.Structure):
+    """``glm_moe_mx_weights``: E4M3 code tensors and their E8M0 scales."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w1", "w1_scale", "w3", "w3_scale", "w2", "w2_scale", "shared_w1", "shared_w1_scale",
+        "shared_w3", "shared_w3_scale", "shared_w2", "shared_w2_scale")]
 
 
 _lib = None
@@ -64,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.glm_moe_forward_traced.argtypes = L.glm_moe_forward.argtypes + [vp]
         L.glm_moe_forward_ex.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
                                          vp, vp, vp, sz, vp, vp]
+        L.glm_moe_forward_mx.argtypes = [pd, po, vp, vp, vp, ctypes.POINTER(MxWeights), i32, f32,
+                                         vp, vp, vp, vp, sz, vp, vp]
         L.glm_moe_dense_workspace_size.argtypes = [pd, po, ctypes.POINTER(sz)]
         L.glm_moe_dense_ffn.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.glm_moe_trace_create.argtypes = [ctypes.POINTER(vp), i32]
@@ -77,7 +86,7 @@ def lib() -> ctypes.CDLL:
         L.glm_moe_version.restype = i32
         for name in ("glm_moe_workspace_size", "glm_moe_workspace_size_ex", "glm_moe_route",
                      "glm_moe_route_ex", "glm_moe_forward", "glm_moe_forward_traced",
-                     "glm_moe_forward_ex", "glm_moe_dense_workspace_size", "glm_moe_dense_ffn",
+                     "glm_moe_forward_ex", "glm_moe_forward_mx", "glm_moe_dense_workspace_size", "glm_moe_dense_ffn",
                      "glm_moe_trace_create", "glm_moe_trace_destroy", "glm_moe_trace_reset",
                      "glm_moe_trace_read"):
             getattr(L, name).restype = i32
@@ -100,9 +109,11 @@ def _dtype_code(t: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
 
 
-def dims(T: int, D: int, E: int, F: int, Fs: int, dtype: torch.dtype) -> Dims:
+def dims(T: int, D: int, E: int, F: int, Fs: int, dtype: torch.dtype,
+         weight: Optional[int] = None) -> Dims:
+    """Layer sizes; ``weight`` overrides the weight dtype code (MXFP8)."""
     c = _dtype_code(dtype)
-    return Dims(T, D, E, F, Fs, c, c)
+    return Dims(T, D, E, F, Fs, c, c if weight is None else weight)
 
 
 def options(n_group: int = 1, topk_group: int = 1, group_topk: int = 0,
@@ -117,9 +128,10 @@ def options(n_group: int = 1, topk_group: int = 1, group_topk: int = 0,
 
 
 def workspace_size(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
-                   dtype: torch.dtype = torch.bfloat16, opts: Optional[Options] = None) -> int:
+                   dtype: torch.dtype = torch.bfloat16, opts: Optional[Options] = None,
+                   weight: Optional[int] = None) -> int:
     n = ctypes.c_size_t(0)
-    _check(lib().glm_moe_workspace_size_ex(ctypes.byref(dims(T, D, E, F, Fs, dtype)),
+    _check(lib().glm_moe_workspace_size_ex(ctypes.byref(dims(T, D, E, F, Fs, dtype, weight)),
                                            None if opts is None else ctypes.byref(opts), top_k,
                                            ctypes.byref(n)), "glm_moe_workspace_size_ex")
     return n.value
@@ -153,8 +165,8 @@ def _stream() -> int:
 
 
 def new_workspace(T, D, E, F, Fs, top_k, dtype, device=None,
-                  opts: Optional[Options] = None) -> torch.Tensor:
-    n = workspace_size(T, D, E, F, Fs, top_k, dtype, opts)
+                  opts: Optional[Options] = None, weight: Optional[int] = None) -> torch.Tensor:
+    n = workspace_size(T, D, E, F, Fs, top_k, dtype, opts, weight)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
 
 
@@ -280,4 +292,51 @@ def dense_ffn(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(),
         None if trace is None else trace.handle)
     _check(st, "glm_moe_dense_ffn")
+    return out
+
+
+def forward_mx(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
+               w1: torch.Tensor, w1_scale: torch.Tensor, w3: torch.Tensor,
+               w3_scale: torch.Tensor, w2: torch.Tensor, w2_scale: torch.Tensor,
+               shared_w1: torch.Tensor, shared_w1_scale: torch.Tensor,
+               shared_w3: torch.Tensor, shared_w3_scale: torch.Tensor,
+               shared_w2: torch.Tensor, shared_w2_scale: torch.Tensor,
+               top_k: int, scale: float, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None,
+               topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+               trace: Optional[Trace] = None, *, n_group: int = 1, topk_group: int = 1,
+               group_topk: int = 0, norm_weight: Optional[torch.Tensor] = None,
+               norm_eps: float = 1e-5, residual: bool = False) -> torch.Tensor:
+    """The layer with MXFP8 expert weights (uint8 E4M3 codes and uint8 E8M0
+    scales, one per 32 elements along each row); x is bfloat16."""
+    T, D = x.shape
+    E, F, _ = w1.shape
+    Fs = shared_w1.shape[0]
+    u8 = torch.uint8
+    d = dims(T, D, E, F, Fs, x.dtype, MXFP8)
+    o = options(n_group, topk_group, group_topk, norm_weight, norm_eps, residual, D)
+    W = MxWeights(
+        _ptr(w1, "w1", u8, (E, F, D)), _ptr(w1_scale, "w1_scale", u8, (E, F, D // 32)),
+        _ptr(w3, "w3", u8, (E, F, D)), _ptr(w3_scale, "w3_scale", u8, (E, F, D // 32)),
+        _ptr(w2, "w2", u8, (E, D, F)), _ptr(w2_scale, "w2_scale", u8, (E, D, F // 32)),
+        _ptr(shared_w1, "shared_w1", u8, (Fs, D)),
+        _ptr(shared_w1_scale, "shared_w1_scale", u8, (Fs, D // 32)),
+        _ptr(shared_w3, "shared_w3", u8, (Fs, D)),
+        _ptr(shared_w3_scale, "shared_w3_scale", u8, (Fs, D // 32)),
+        _ptr(shared_w2, "shared_w2", u8, (D, Fs)),
+        _ptr(shared_w2_scale, "shared_w2_scale", u8, (D, Fs // 32)))
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(T, D, E, F, Fs, top_k, x.dtype, x.device, o, MXFP8)
+    st = lib().glm_moe_forward_mx(
+        ctypes.byref(d), ctypes.byref(o), _ptr(x, "x", torch.bfloat16, (T, D)),
+        _ptr(router_w, "router_w", torch.float32, (E, D)),
+        _ptr(corr_bias, "corr_bias", torch.float32, (E,)), ctypes.byref(W), top_k,
+        float(scale), _ptr(out, "out", torch.float32, (T, D)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, top_k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, top_k)),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(),
+        None if trace is None else trace.handle)
+    _check(st, "glm_moe_forward_mx")
     return out

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libglm_moe.so")
-SOURCES = ["router.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip", "block.hip",
-           "glm_moe.hip"]
+SOURCES = ["router.hip", "permute.hip", "gemm_bf16.hip", "gemm_mx.hip", "gemm_f32.hip",
+           "block.hip", "glm_moe.hip"]
 ARCH = "gfx950"
 
 

@@ -117,6 +117,46 @@ hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s);
 hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, const void* residual,
                           bool res_bf16, hipStream_t s);
 
+// MXFP8 grouped GEMMs (OCP MX: E4M3 codes, one E8M0 scale per 32 elements
+// along the contraction dimension; scale arrays are [rows][K/32] bytes).
+struct MxGateUpArgs {
+  const uint8_t* xq;           // [T][D]   layer input, quantised per token
+  const uint8_t* xs;           // [T][D/32]
+  const int32_t* row_assign;
+  const int32_t* offsets;
+  const uint8_t* w1; const uint8_t* w1s;   // [E][F][D], [E][F][D/32]
+  const uint8_t* w3; const uint8_t* w3s;
+  const uint8_t* sw1; const uint8_t* sw1s; // [Fs][D], [Fs][D/32]
+  const uint8_t* sw3; const uint8_t* sw3s;
+  const TileDesc* desc;
+  const int32_t* desc_count;
+  uint8_t* H; uint8_t* Hsc;    // [T*k][F], [T*k][F/32]: gated hidden rows, quantised
+  uint8_t* Hs; uint8_t* Hssc;  // [T][Fs], [T][Fs/32]
+  int T, D, E, F, Fs, k;
+  int grid;
+};
+struct MxDownArgs {
+  const uint8_t* H; const uint8_t* Hsc;
+  const uint8_t* Hs; const uint8_t* Hssc;
+  const int32_t* row_assign;
+  const int32_t* offsets;
+  const uint8_t* w2; const uint8_t* w2s;   // [E][D][F], [E][D][F/32]
+  const uint8_t* sw2; const uint8_t* sw2s; // [D][Fs], [D][Fs/32]
+  const float* topk_w;
+  const TileDesc* desc;
+  const int32_t* desc_count;
+  float* Y;                    // as DownArgs
+  int T, D, E, F, Fs, k;
+  int grid;
+};
+// x (bf16 [T][D]) -> MXFP8 codes [T][D] and scales [T][D/32].
+hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int T, int D,
+                              hipStream_t s);
+// Tile shape of an MXFP8 grouped GEMM launch (same `wide` rule as gemm_shape).
+GemmShape gemm_shape_mx(double rows_per_group, bool wide);
+hipError_t launch_gateup_mx(const MxGateUpArgs& a, GemmShape sh, hipStream_t s);
+hipError_t launch_down_mx(const MxDownArgs& a, GemmShape sh, hipStream_t s);
+
 // Pre-norm block: out = h / sqrt(mean(h^2) + eps) * w per row, computed in
 // fp64 and rounded once to the activation dtype (bf16 or fp32).
 hipError_t launch_rmsnorm(const void* h, const float* w, void* out, int T, int D, float eps,
@@ -142,6 +182,17 @@ hipError_t launch_shared_combine_f32(const F32Args& a, hipStream_t s);
 __host__ __device__ inline int y_row(int a, int k) { return (a / k) * (k + 1) + a % k; }
 
 // ------------------------------------------------------------- helpers
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate: vector-memory count N, other counters left alone.
+#define GLM_VMCNT(N) (((N) & 0xF) | (((N) >> 4) << 14) | (7 << 4) | (0xF << 8))
+
+// Workgroup barrier after this wave's LDS operations have completed (and
+// nothing else: outstanding global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 

@@ -40,15 +40,7 @@ namespace gemm {
 
 enum Mode { GATE_UP = 0, DOWN = 1 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// s_waitcnt immediate: vector-memory count N, other counters left alone.
-#define GLM_VMCNT(N) (((N) & 0xF) | (((N) >> 4) << 14) | (7 << 4) | (0xF << 8))
-
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Physical 16-byte chunk of logical chunk c in row r: c ^ swz(r).  Rows r and
 // r+1..r+15 read at one logical chunk land on distinct banks for both 8- and

@@ -31,7 +31,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Workspace regions (byte offsets) and launch parameters of one call.
 struct Plan {
   int T, D, E, F, Fs, k;
-  bool bf16;
+  bool bf16;         // bf16 activations
+  bool mx;           // MXFP8 expert weights (H, Hs hold E4M3 codes)
   bool dense;        // no routed experts: the shared group only
   int ntiles;        // 64-token routing tiles
   int ksplit, kchunk;
@@ -42,7 +43,7 @@ struct Plan {
   float norm_eps;
   bool add_residual;
   size_t xnorm, partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
-      dn_desc, row_assign, H, Hs, Y;
+      dn_desc, row_assign, H, Hs, Y, xq, xs, Hsc, Hssc;
   size_t total;
 };
 
@@ -100,13 +101,20 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
     if (top_k < 1 || top_k > kmax)
       return fail(GLM_MOE_EINVAL, "top_k=%d outside [1, %d]", top_k, kmax);
   }
-  if (d->act_dtype != d->weight_dtype ||
-      (d->act_dtype != GLM_MOE_F32 && d->act_dtype != GLM_MOE_BF16))
-    return fail(GLM_MOE_EUNSUPPORTED, "dtype pair act=%d weight=%d (supported: f32/f32, bf16/bf16)",
+  const bool mx = d->act_dtype == GLM_MOE_BF16 && d->weight_dtype == GLM_MOE_MXFP8;
+  if (!mx && (d->act_dtype != d->weight_dtype ||
+              (d->act_dtype != GLM_MOE_F32 && d->act_dtype != GLM_MOE_BF16)))
+    return fail(GLM_MOE_EUNSUPPORTED,
+                "dtype pair act=%d weight=%d (supported: f32/f32, bf16/bf16, bf16/mxfp8)",
                 d->act_dtype, d->weight_dtype);
+  if (mx && dense)
+    return fail(GLM_MOE_EUNSUPPORTED, "the dense FFN takes f32 or bf16 weights");
   const bool bf16 = d->act_dtype == GLM_MOE_BF16;
   if (bf16 && (d->D % 64 || d->F_shared % 64 || (!dense && d->F % 64)))
     return fail(GLM_MOE_EUNSUPPORTED, "bf16 path needs D, F, F_shared multiples of 64 (D=%d F=%d Fs=%d)",
+                d->D, d->F, d->F_shared);
+  if (mx && (d->D % 128 || d->F % 128 || d->F_shared % 128))
+    return fail(GLM_MOE_EUNSUPPORTED, "MXFP8 path needs D, F, F_shared multiples of 128 (D=%d F=%d Fs=%d)",
                 d->D, d->F, d->F_shared);
   if ((long long)d->T * (dense ? 1 : top_k) > (1ll << 30))
     return fail(GLM_MOE_EUNSUPPORTED, "T*top_k=%lld too large", (long long)d->T * top_k);
@@ -120,6 +128,7 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   P.F = dense ? 0 : d->F;
   P.k = dense ? 0 : top_k;
   P.bf16 = bf16;
+  P.mx = mx;
   const int T = P.T, A = T * P.k;
   P.ntiles = cdiv(T, kTokTile);
 
@@ -135,8 +144,8 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
     P.ksplit = cdiv(P.D, P.kchunk);
     const double per_group = dense ? (double)T : (double)A / P.E;
     const bool wide_gu = (dense || P.F % 128 == 0) && P.Fs % 128 == 0;
-    P.gu = gemm_shape(per_group, wide_gu);
-    P.dn = gemm_shape(per_group, P.D % 256 == 0);
+    P.gu = mx ? gemm_shape_mx(per_group, wide_gu) : gemm_shape(per_group, wide_gu);
+    P.dn = mx ? gemm_shape_mx(per_group, P.D % 256 == 0) : gemm_shape(per_group, P.D % 256 == 0);
     // routed tiles, then the shared (or dense) group's tiles (group E)
     P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) +
                cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
@@ -149,6 +158,7 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   }
 
   const size_t act = bf16 ? 2 : 4;
+  const size_t hid = mx ? 1 : act;  // bytes per hidden element (E4M3 codes for MXFP8)
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   P.xnorm = take(P.norm_weight ? (size_t)T * P.D * act : 0);
@@ -164,9 +174,13 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   P.gu_desc = take((size_t)P.gu_cap * sizeof(TileDesc));
   P.dn_desc = take((size_t)P.dn_cap * sizeof(TileDesc));
   P.row_assign = take((size_t)A * 4);
-  P.H = take((size_t)A * P.F * act);
-  P.Hs = take((size_t)T * P.Fs * act);
+  P.H = take((size_t)A * P.F * hid);
+  P.Hs = take((size_t)T * P.Fs * hid);
   P.Y = take((size_t)T * (P.k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
+  P.xq = take(mx ? (size_t)T * P.D : 0);        // MXFP8 input codes and scales
+  P.xs = take(mx ? (size_t)T * P.D / 32 : 0);
+  P.Hsc = take(mx ? (size_t)A * P.F / 32 : 0);  // MXFP8 hidden-row scales
+  P.Hssc = take(mx ? (size_t)T * P.Fs / 32 : 0);
   P.total = T == 0 ? 0 : o;
   return GLM_MOE_OK;
 }
@@ -252,11 +266,19 @@ int run_topk(const Plan& P, const float* corr_bias, float scale, int32_t* idx, f
   return GLM_MOE_OK;
 }
 
+// Expert weights of one call (the scales only for MXFP8).
+struct Weights {
+  const void* w1; const void* w3; const void* w2;
+  const void* sw1; const void* sw3; const void* sw2;
+  const uint8_t* w1s = nullptr; const uint8_t* w3s = nullptr; const uint8_t* w2s = nullptr;
+  const uint8_t* sw1s = nullptr; const uint8_t* sw3s = nullptr; const uint8_t* sw2s = nullptr;
+};
+
 // Everything after the routing: permutation, grouped GEMMs, combine.
 int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, float* wts,
-                const void* w1, const void* w3, const void* w2, const void* shared_w1,
-                const void* shared_w3, const void* shared_w2, float* out, void* ws,
-                hipStream_t s, Recorder& rec) {
+                const Weights& W, float* out, void* ws, hipStream_t s, Recorder& rec) {
+  const void *w1 = W.w1, *w3 = W.w3, *w2 = W.w2;
+  const void *shared_w1 = W.sw1, *shared_w3 = W.sw3, *shared_w2 = W.sw2;
   uint64_t* masks = at<uint64_t>(ws, P.masks);
   int32_t* tile_base = at<int32_t>(ws, P.tile_base);
   int32_t* counts = at<int32_t>(ws, P.counts);
@@ -281,7 +303,39 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));
   if (!P.dense) GLM_HIP(launch_scatter(idx, masks, tile_base, P.T, P.E, P.k, row_assign, s));
 
-  if (P.bf16) {
+  if (P.mx) {
+    uint8_t* xq = at<uint8_t>(ws, P.xq);
+    uint8_t* xs = at<uint8_t>(ws, P.xs);
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
+    GLM_HIP(launch_quantize_mx(static_cast<const bf16_t*>(xin), xq, xs, P.T, P.D, s));
+    MxGateUpArgs ga{};
+    ga.xq = xq; ga.xs = xs;
+    ga.row_assign = row_assign; ga.offsets = offsets;
+    ga.w1 = static_cast<const uint8_t*>(w1); ga.w1s = W.w1s;
+    ga.w3 = static_cast<const uint8_t*>(w3); ga.w3s = W.w3s;
+    ga.sw1 = static_cast<const uint8_t*>(shared_w1); ga.sw1s = W.sw1s;
+    ga.sw3 = static_cast<const uint8_t*>(shared_w3); ga.sw3s = W.sw3s;
+    ga.desc = gu_desc; ga.desc_count = gu_count;
+    ga.H = at<uint8_t>(ws, P.H); ga.Hsc = at<uint8_t>(ws, P.Hsc);
+    ga.Hs = at<uint8_t>(ws, P.Hs); ga.Hssc = at<uint8_t>(ws, P.Hssc);
+    ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
+    ga.grid = cdiv(P.gu_cap, kXcds) * kXcds;
+    GLM_HIP(launch_gateup_mx(ga, P.gu, s));
+
+    MxDownArgs da{};
+    da.H = ga.H; da.Hsc = ga.Hsc; da.Hs = ga.Hs; da.Hssc = ga.Hssc;
+    da.row_assign = row_assign; da.offsets = offsets;
+    da.w2 = static_cast<const uint8_t*>(w2); da.w2s = W.w2s;
+    da.sw2 = static_cast<const uint8_t*>(shared_w2); da.sw2s = W.sw2s;
+    da.topk_w = wts; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
+    da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
+    da.grid = cdiv(P.dn_cap, kXcds) * kXcds;
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
+    GLM_HIP(launch_down_mx(da, P.dn, s));
+
+    GLM_HIP(rec.mark(GLM_MOE_STAGE_SHARED_COMBINE));
+    GLM_HIP(launch_combine(Y, out, P.T, P.D, P.k, residual, true, s));
+  } else if (P.bf16) {
     GateUpArgs ga{};
     ga.x = static_cast<const bf16_t*>(xin);
     ga.row_assign = row_assign; ga.offsets = offsets;
@@ -326,6 +380,26 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   }
   GLM_HIP(rec.mark(GLM_MOE_NUM_STAGES));
   return GLM_MOE_OK;
+}
+
+// The whole layer after argument checks: [norm ->] router -> top-k -> experts.
+int run_layer(const Plan& P, const void* x, const float* router_w, const float* corr_bias,
+              const Weights& W, float scale, float* out, int32_t* topk_idx_out,
+              float* topk_w_out, void* workspace, hipStream_t stream, glm_moe_trace* trace) {
+  int st;
+  void* ws = workspace;
+  hipStream_t s = stream;
+  Recorder rec(trace, s);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, P.idx);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, P.w);
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_NORM));
+  const void* xin;
+  if ((st = layer_input(P, x, ws, s, &xin))) return st;
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
+  if ((st = run_router(P, xin, router_w, ws, s))) return st;
+  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
+  if ((st = run_topk(P, corr_bias, scale, idx, wts, ws, s))) return st;
+  return run_experts(P, x, xin, idx, wts, W, out, ws, s, rec);
 }
 
 int check_route_args(const void* x, const float* router_w, const float* corr_bias) {
@@ -398,22 +472,50 @@ int glm_moe_forward_ex(const glm_moe_dims* d, const glm_moe_options* opts, const
     return fail(GLM_MOE_EINVAL, "topk_idx_out is not 16-byte aligned");
   if (topk_w_out && misaligned(topk_w_out))
     return fail(GLM_MOE_EINVAL, "topk_w_out is not 16-byte aligned");
+  if (P.mx)
+    return fail(GLM_MOE_EINVAL, "MXFP8 weights take glm_moe_forward_mx (they carry scales)");
   if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+  Weights W{w1, w3, w2, shared_w1, shared_w3, shared_w2};
+  return run_layer(P, x, router_w, corr_bias, W, scale, out, topk_idx_out, topk_w_out,
+                   workspace, stream, trace);
+}
 
-  void* ws = workspace;
-  hipStream_t s = stream;
-  Recorder rec(trace, s);
-  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, P.idx);
-  float* wts = topk_w_out ? topk_w_out : at<float>(ws, P.w);
-  GLM_HIP(rec.mark(GLM_MOE_STAGE_NORM));
-  const void* xin;
-  if ((st = layer_input(P, x, ws, s, &xin))) return st;
-  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
-  if ((st = run_router(P, xin, router_w, ws, s))) return st;
-  GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
-  if ((st = run_topk(P, corr_bias, scale, idx, wts, ws, s))) return st;
-  return run_experts(P, x, xin, idx, wts, w1, w3, w2, shared_w1, shared_w3, shared_w2, out, ws,
-                     s, rec);
+int glm_moe_forward_mx(const glm_moe_dims* d, const glm_moe_options* opts, const void* x,
+                       const float* router_w, const float* corr_bias, const glm_moe_mx_weights* w,
+                       int top_k, float scale, float* out, int32_t* topk_idx_out,
+                       float* topk_w_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, glm_moe_trace* trace) {
+  Plan P;
+  int st = make_plan(d, top_k, opts, false, &P);
+  if (st) return st;
+  if (!P.mx)
+    return fail(GLM_MOE_EINVAL, "glm_moe_forward_mx needs act_dtype BF16 and weight_dtype MXFP8");
+  if (P.T == 0) return GLM_MOE_OK;
+  if (!w) return fail(GLM_MOE_EINVAL, "weights is null");
+  if ((st = check_route_args(x, router_w, corr_bias))) return st;
+  if ((st = check_ptr(w->w1, "w1")) || (st = check_ptr(w->w1_scale, "w1_scale")) ||
+      (st = check_ptr(w->w3, "w3")) || (st = check_ptr(w->w3_scale, "w3_scale")) ||
+      (st = check_ptr(w->w2, "w2")) || (st = check_ptr(w->w2_scale, "w2_scale")) ||
+      (st = check_ptr(w->shared_w1, "shared_w1")) ||
+      (st = check_ptr(w->shared_w1_scale, "shared_w1_scale")) ||
+      (st = check_ptr(w->shared_w3, "shared_w3")) ||
+      (st = check_ptr(w->shared_w3_scale, "shared_w3_scale")) ||
+      (st = check_ptr(w->shared_w2, "shared_w2")) ||
+      (st = check_ptr(w->shared_w2_scale, "shared_w2_scale")) || (st = check_ptr(out, "out")))
+    return st;
+  if (topk_idx_out && misaligned(topk_idx_out))
+    return fail(GLM_MOE_EINVAL, "topk_idx_out is not 16-byte aligned");
+  if (topk_w_out && misaligned(topk_w_out))
+    return fail(GLM_MOE_EINVAL, "topk_w_out is not 16-byte aligned");
+  if ((st = check_ws(P, workspace, workspace_bytes))) return st;
+  Weights W{w->w1, w->w3, w->w2, w->shared_w1, w->shared_w3, w->shared_w2,
+            static_cast<const uint8_t*>(w->w1_scale), static_cast<const uint8_t*>(w->w3_scale),
+            static_cast<const uint8_t*>(w->w2_scale),
+            static_cast<const uint8_t*>(w->shared_w1_scale),
+            static_cast<const uint8_t*>(w->shared_w3_scale),
+            static_cast<const uint8_t*>(w->shared_w2_scale)};
+  return run_layer(P, x, router_w, corr_bias, W, scale, out, topk_idx_out, topk_w_out,
+                   workspace, stream, trace);
 }
 
 int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* router_w,
@@ -466,8 +568,8 @@ int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* opts, const 
   if ((st = layer_input(P, x, workspace, stream, &xin))) return st;
   GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_LOGITS));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_ROUTER_TOPK));
-  return run_experts(P, x, xin, nullptr, nullptr, nullptr, nullptr, nullptr, w1, w3, w2, out,
-                     workspace, stream, rec);
+  Weights W{nullptr, nullptr, nullptr, w1, w3, w2};
+  return run_experts(P, x, xin, nullptr, nullptr, W, out, workspace, stream, rec);
 }
 
 int glm_moe_trace_create(glm_moe_trace** trace, int max_calls) {

@@ -294,3 +294,62 @@ def test_dense_argument_checks():
     d0 = Dims(0, 128, 0, 0, 64, glm.BF16, glm.BF16)
     assert L.glm_moe_dense_ffn(ctypes.byref(d0), None, 0, 0, 0, 0, 0, 0, 0, None,
                                None) == glm.OK
+
+
+# ----------------------------------------------------------- MXFP8 weights
+
+from sparse_moe_transformer_glm_amd._lib import MxWeights  # noqa: E402
+
+
+def _mx_dims(T=64, D=6144, E=256, F=2048, Fs=2048):
+    return Dims(T, D, E, F, Fs, glm.BF16, glm.MXFP8)
+
+
+def test_mx_workspace_and_shape_rules():
+    n = ctypes.c_size_t(0)
+    L = glm.lib()
+    assert L.glm_moe_workspace_size_ex(ctypes.byref(_mx_dims()), None, 8, ctypes.byref(n)) == glm.OK
+    # hidden rows as 1-byte codes plus a scale per 32: smaller than bf16 hidden rows
+    _, nb = _ws(64, 6144, 256, 2048, 2048, 8)
+    assert 0 < n.value < nb
+    for bad in (_mx_dims(D=6144 + 64), _mx_dims(F=2048 + 64), _mx_dims(Fs=2048 + 64)):
+        assert L.glm_moe_workspace_size_ex(ctypes.byref(bad), None, 8,
+                                           ctypes.byref(n)) == glm.EUNSUPPORTED
+    f32mx = Dims(64, 6144, 256, 2048, 2048, glm.F32, glm.MXFP8)
+    assert L.glm_moe_workspace_size_ex(ctypes.byref(f32mx), None, 8,
+                                       ctypes.byref(n)) == glm.EUNSUPPORTED
+    dense = Dims(64, 6144, 0, 0, 2048, glm.BF16, glm.MXFP8)
+    assert L.glm_moe_dense_workspace_size(ctypes.byref(dense), None,
+                                          ctypes.byref(n)) == glm.EUNSUPPORTED
+
+
+def _forward_mx(d, W, ws=FAKE, ws_bytes=1 << 40, k=8, x=FAKE, out=FAKE):
+    return glm.lib().glm_moe_forward_mx(ctypes.byref(d), None, x, FAKE, FAKE,
+                                        None if W is None else ctypes.byref(W), k, 2.5, out,
+                                        None, None, ws, ws_bytes, None, None)
+
+
+def test_forward_mx_argument_checks():
+    d = _mx_dims()
+    names = [f for f, _ in MxWeights._fields_]
+    good = MxWeights(*([FAKE] * len(names)))
+    assert _forward_mx(d, None) == glm.EINVAL
+    for i in range(len(names)):
+        vals = [FAKE] * len(names)
+        vals[i] = 0
+        assert _forward_mx(d, MxWeights(*vals)) == glm.EINVAL, names[i]
+        vals[i] = FAKE + 4
+        assert _forward_mx(d, MxWeights(*vals)) == glm.EINVAL, names[i]
+    assert _forward_mx(d, good, x=0) == glm.EINVAL
+    assert _forward_mx(d, good, out=0) == glm.EINVAL
+    n = ctypes.c_size_t(0)
+    glm.lib().glm_moe_workspace_size_ex(ctypes.byref(d), None, 8, ctypes.byref(n))
+    assert _forward_mx(d, good, ws_bytes=n.value - 1) == glm.EWORKSPACE
+    # bf16 weights through the MXFP8 entry, MXFP8 weights through the bf16 one
+    bf = Dims(64, 6144, 256, 2048, 2048, glm.BF16, glm.BF16)
+    assert _forward_mx(bf, good) == glm.EINVAL
+    ptrs = [FAKE] * 10
+    assert glm.lib().glm_moe_forward(ctypes.byref(d), *ptrs[:9], 8, 2.5, ptrs[9], None, None,
+                                     FAKE, 1 << 40, None) == glm.EINVAL
+    # zero tokens: no-op
+    assert _forward_mx(_mx_dims(T=0), None, x=0, out=0) == glm.OK

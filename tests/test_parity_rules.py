@@ -102,3 +102,126 @@ def test_group_near_tie_swap_is_excused():
     W = np.diag(np.log(beta_target / (1 - beta_target)))
     rep = parity.compare_routing(other, r.weight, x, W, b, 4, 1.0, **GROUPS)
     assert rep.invalid == [0]
+
+
+# ------------------------------------------------------- MXFP8 rounding ties
+
+from oracle import mx  # noqa: E402
+
+
+def _mx_layer(seed=9, T=48, D=256, E=8, F=128, k=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, D))
+    W = rng.standard_normal((E, D)) * 0.1
+    b = rng.standard_normal(E) * 0.01
+    q = lambda a: mx.quantize(a)
+    ex = {e: (q(rng.standard_normal((F, D)) / 16), q(rng.standard_normal((F, D)) / 16),
+              q(rng.standard_normal((D, F)) / 11)) for e in range(E)}
+    sh = (q(rng.standard_normal((F, D)) / 16), q(rng.standard_normal((F, D)) / 16),
+          q(rng.standard_normal((D, F)) / 11))
+    return x, W, b, ex, sh, k
+
+
+def _fp32_mx_layer(x, r, ex, sh):
+    """The MXFP8 layer with the expert products in fp32 (a stand-in for a GPU
+    result: same quantisation rules, hidden values rounded from fp32)."""
+    xq = mx.fake_quantize(x).astype(np.float32)
+    def mlp(rows, w1, w3, w2):
+        W1, W3, W2 = (mx.dequantize(*w).astype(np.float32) for w in (w1, w3, w2))
+        g, u = rows @ W1.T, rows @ W3.T
+        h = (g / (np.float32(1) + np.exp(-g)) * u).astype(np.float32)
+        return mx.fake_quantize(h.astype(np.float64)) @ W2.T.astype(np.float64)
+    out = np.zeros(x.shape)
+    for e in np.unique(r.idx):
+        tok, slot = np.nonzero(r.idx == e)
+        out[tok] += r.weight[tok, slot][:, None] * mlp(xq[tok], *ex[e])
+    return out + mlp(xq, *sh)
+
+
+def _layer_from_hidden(x, r, ex, sh, edit=None):
+    """The MXFP8 layer evaluated with the oracle's numbers, except that
+    ``edit(slot_key, hq)`` may change the quantised hidden rows of a slot."""
+    xq = mx.fake_quantize(x)
+    def mlp(key, rows, w1, w3, w2):
+        W1, W3, W2 = (mx.dequantize(*w) for w in (w1, w3, w2))
+        h = (lambda g, u: g / (1 + np.exp(-g)) * u)(rows @ W1.T, rows @ W3.T)
+        hq = mx.fake_quantize(h)
+        if edit is not None:
+            hq = edit(key, h, hq)
+        return hq @ W2.T
+    out = np.zeros(x.shape)
+    for e in np.unique(r.idx):
+        tok, slot = np.nonzero(r.idx == e)
+        out[tok] += r.weight[tok, slot][:, None] * mlp(int(e), xq[tok], *ex[e])
+    return out + mlp("shared", xq, *sh)
+
+
+def test_mx_explain_accepts_equal_and_fp32_results():
+    x, W, b, ex, sh, k = _mx_layer()
+    ref, r = oracle.forward_mx(x, W, b, lambda e: ex[e], sh, k, 2.5)
+    same = parity.mx_explain(ref, ref, x, r, lambda e: ex[e], sh)
+    assert same.violations == 0 and same.flips == 0 and same.mean_rel == 0
+    got = _fp32_mx_layer(x, r, ex, sh)
+    rep = parity.mx_explain(got, ref, x, r, lambda e: ex[e], sh)
+    assert rep.violations == 0, rep
+
+
+def _midpoint_element(h, hq):
+    """(row, col) of the hidden value closest (relatively) to an E4M3 midpoint,
+    and the value with its rounding moved to the other neighbour."""
+    n, F = h.shape
+    s = mx.block_exponent(np.abs(h.reshape(n, F // 32, 32)).max(-1)).repeat(32, axis=1)
+    y = np.abs(h) / np.exp2(s)
+    lo, hi = parity._e4m3_neighbours(y)
+    dist = np.abs(y - (lo + hi) / 2) / (hi - lo)
+    dist[np.abs(h) == np.abs(h.reshape(n, F // 32, 32)).max(-1).repeat(32, axis=1)] = np.inf
+    i, f = np.unravel_index(np.argmin(dist), dist.shape)
+    chosen = np.abs(hq[i, f]) / 2.0 ** s[i, f]
+    alt = hi[i, f] if chosen == lo[i, f] else lo[i, f]
+    return i, f, np.sign(h[i, f]) * alt * 2.0 ** s[i, f], dist[i, f]
+
+
+def test_mx_explain_takes_a_flip_at_a_midpoint_and_nothing_else():
+    x, W, b, ex, sh, k = _mx_layer(seed=11)
+    ref, r = oracle.forward_mx(x, W, b, lambda e: ex[e], sh, k, 2.5)
+    picked = {}
+
+    def flip_near(key, h, hq):
+        if key != "shared":
+            return hq
+        i, f, v, dist = _midpoint_element(h, hq)
+        picked["dist"] = dist
+        hq = hq.copy()
+        hq[i, f] = v
+        return hq
+
+    got = _layer_from_hidden(x, r, ex, sh, flip_near)
+    rep = parity.mx_explain(got, ref, x, r, lambda e: ex[e], sh)
+    assert picked["dist"] < 1e-3
+    assert rep.violations == 0 and rep.flips == 1, rep
+
+    def flip_far(key, h, hq):
+        if key != "shared":
+            return hq
+        hq = hq.copy()
+        # the rounding of a value far from any midpoint moved by one step
+        n, F = h.shape
+        s = mx.block_exponent(np.abs(h.reshape(n, F // 32, 32)).max(-1)).repeat(32, axis=1)
+        y = np.abs(h) / np.exp2(s)
+        lo, hi = parity._e4m3_neighbours(y)
+        dist = np.abs(y - (lo + hi) / 2) / (hi - lo)
+        i, f = np.unravel_index(np.argmax(np.where(np.abs(h) > 0.1, dist, -1)), dist.shape)
+        hq[i, f] += np.sign(h[i, f]) * (hi[i, f] - lo[i, f]) * 2.0 ** s[i, f]
+        return hq
+
+    bad = _layer_from_hidden(x, r, ex, sh, flip_far)
+    assert parity.mx_explain(bad, ref, x, r, lambda e: ex[e], sh).violations > 0
+
+
+def test_mx_explain_flags_small_output_errors():
+    x, W, b, ex, sh, k = _mx_layer(seed=12)
+    ref, r = oracle.forward_mx(x, W, b, lambda e: ex[e], sh, k, 2.5)
+    bad = ref.copy()
+    rms = np.sqrt((ref ** 2).mean())
+    bad[3, 7] += 1e-2 * rms
+    assert parity.mx_explain(bad, ref, x, r, lambda e: ex[e], sh).violations == 1

@@ -38,17 +38,34 @@ class DeviceLayer:
     sw3: torch.Tensor
     sw2: torch.Tensor
 
+    # MXFP8 scales (None for f32 / bf16 weights)
+    w1s: Optional[torch.Tensor] = None
+    w3s: Optional[torch.Tensor] = None
+    w2s: Optional[torch.Tensor] = None
+    sw1s: Optional[torch.Tensor] = None
+    sw3s: Optional[torch.Tensor] = None
+    sw2s: Optional[torch.Tensor] = None
+
     def args(self):
-        return (self.x, self.router_w, self.corr_bias, self.w1, self.w3, self.w2,
-                self.sw1, self.sw3, self.sw2)
+        """Positional tensor arguments of ``forward`` (or ``forward_mx``)."""
+        if self.w1s is None:
+            return (self.x, self.router_w, self.corr_bias, self.w1, self.w3, self.w2,
+                    self.sw1, self.sw3, self.sw2)
+        return (self.x, self.router_w, self.corr_bias, self.w1, self.w1s, self.w3, self.w3s,
+                self.w2, self.w2s, self.sw1, self.sw1s, self.sw3, self.sw3s, self.sw2, self.sw2s)
+
+    def with_x(self, x: torch.Tensor, corr_bias: Optional[torch.Tensor] = None,
+               w: Optional[Workload] = None) -> "DeviceLayer":
+        """The same weights with another input batch (and bias)."""
+        return dataclasses.replace(self, x=x, w=self.w if w is None else w,
+                                   corr_bias=self.corr_bias if corr_bias is None else corr_bias)
 
 
 def upload_layer(L: HostLayer, device="cuda") -> DeviceLayer:
-    return DeviceLayer(L.w, to_device(L.x, device), to_device(L.router_w, device),
-                       to_device(L.corr_bias, device), to_device(L.w1, device),
-                       to_device(L.w3, device), to_device(L.w2, device),
-                       to_device(L.sw1, device), to_device(L.sw3, device),
-                       to_device(L.sw2, device))
+    t = lambda a: None if a is None else to_device(a, device)
+    return DeviceLayer(L.w, t(L.x), t(L.router_w), t(L.corr_bias), t(L.w1), t(L.w3), t(L.w2),
+                       t(L.sw1), t(L.sw3), t(L.sw2), t(L.w1s), t(L.w3s), t(L.w2s), t(L.sw1s),
+                       t(L.sw3s), t(L.sw2s))
 
 
 def stream_layer(w: Workload, device="cuda", keep_host: bool = False,
@@ -56,30 +73,42 @@ def stream_layer(w: Workload, device="cuda", keep_host: bool = False,
     """Draw the layer expert by expert straight into device tensors.
 
     Returns ``(DeviceLayer, HostLayer or None)``; with ``keep_host`` the host
-    copy (bf16 bits) is kept for the oracle.
+    copy (bf16 bits, or MXFP8 codes and scales) is kept for the oracle.
     """
-    dt = torch_dtype(w)
-    w1 = torch.empty((w.E, w.F, w.D), dtype=dt, device=device)
-    w3 = torch.empty((w.E, w.F, w.D), dtype=dt, device=device)
-    w2 = torch.empty((w.E, w.D, w.F), dtype=dt, device=device)
+    mx = w.dtype == "mxfp8"
+    dt = torch.uint8 if mx else torch_dtype(w)
+    et = np.uint8 if mx else (np.float32 if w.dtype == "f32" else np.uint16)
+    shapes = {"w1": (w.E, w.F, w.D), "w3": (w.E, w.F, w.D), "w2": (w.E, w.D, w.F)}
+    if mx:
+        shapes.update(w1s=(w.E, w.F, w.D // 32), w3s=(w.E, w.F, w.D // 32),
+                      w2s=(w.E, w.D, w.F // 32))
+    dev_t = {k: torch.empty(v, dtype=dt, device=device) for k, v in shapes.items()}
+    host_t = {k: np.empty(v, et) for k, v in shapes.items()} if keep_host else None
+    for e, parts in iter_experts(w, threads):
+        if mx:
+            (a, a_s), (b, b_s), (c, c_s) = parts
+            vals = dict(w1=a, w3=b, w2=c, w1s=a_s, w3s=b_s, w2s=c_s)
+        else:
+            vals = dict(zip(("w1", "w3", "w2"), parts))
+        for k, v in vals.items():
+            dev_t[k][e].copy_(to_device(v, "cpu"))
+            if keep_host:
+                host_t[k][e] = v
+    sh = make_shared(w)
+    x, rw, cb = make_x(w), make_router_w(w), make_corr_bias(w)
+    if mx:
+        (sw1, sw1s), (sw3, sw3s), (sw2, sw2s) = sh
+        sc = [sw1s, sw3s, sw2s]
+    else:
+        sw1, sw3, sw2 = sh
+        sc = [None, None, None]
+    t = lambda a: None if a is None else to_device(a, device)
+    dev = DeviceLayer(w, t(x), t(rw), t(cb), dev_t["w1"], dev_t["w3"], dev_t["w2"], t(sw1),
+                      t(sw3), t(sw2), dev_t.get("w1s"), dev_t.get("w3s"), dev_t.get("w2s"),
+                      t(sc[0]), t(sc[1]), t(sc[2]))
     host = None
     if keep_host:
-        et = np.float32 if w.dtype == "f32" else np.uint16
-        hw1 = np.empty((w.E, w.F, w.D), et)
-        hw3 = np.empty((w.E, w.F, w.D), et)
-        hw2 = np.empty((w.E, w.D, w.F), et)
-    for e, (a, b, c) in iter_experts(w, threads):
-        w1[e].copy_(to_device(a, "cpu"))
-        w3[e].copy_(to_device(b, "cpu"))
-        w2[e].copy_(to_device(c, "cpu"))
-        if keep_host:
-            hw1[e], hw3[e], hw2[e] = a, b, c
-    sw1, sw3, sw2 = make_shared(w)
-    x, rw, cb = make_x(w), make_router_w(w), make_corr_bias(w)
-    dev = DeviceLayer(w, to_device(x, device), to_device(rw, device), to_device(cb, device),
-                      w1, w3, w2, to_device(sw1, device), to_device(sw3, device),
-                      to_device(sw2, device))
-    if keep_host:
-        host = HostLayer(w, x, rw, cb, hw1, hw3, hw2, sw1, sw3, sw2)
+        host = HostLayer(w, x, rw, cb, host_t["w1"], host_t["w3"], host_t["w2"], sw1, sw3, sw2,
+                         host_t.get("w1s"), host_t.get("w3s"), host_t.get("w2s"), *sc)
     torch.cuda.synchronize()
     return dev, host
