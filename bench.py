@@ -23,6 +23,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s @GLM-5.2 shape (T=64 decode, T=8192 prefill); % roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gate_up_glm.json")
 KERNEL_SOURCES = ("gemm_bf16.hip", "common.h")
@@ -58,7 +59,7 @@ def algorithmic(w, counts):
     """Work the method itself needs for one call, from the realised routing."""
     T, D, E, k, F, Fs = w.T, w.D, w.E, w.k, w.F, w.Fs
     n_active = int((counts > 0).sum())
-    wb = 2  # bf16 weight bytes
+    wb = 1 + 1 / 32 if w.dtype == "mxfp8" else 2  # weight bytes per element (MXFP8: + scales)
     f = {
         # routed and shared gate/up (one launch)
         "gate_up": 2.0 * T * k * 2 * F * D + 2.0 * T * 2 * Fs * D,
@@ -106,13 +107,14 @@ def time_layer(glm, torch, dev, w, steps, warmup, ws, **opts):
     scale = opts.pop("scale", w.scale)
     x = opts.pop("x", args[0])
     args = (x,) + tuple(args[1:])
+    fwd = glm.forward_mx if w.dtype == "mxfp8" else glm.forward
 
     def call(tr):
-        glm.forward(*args, w.k, scale, out=out, workspace=ws, trace=tr, **opts)
+        fwd(*args, w.k, scale, out=out, workspace=ws, trace=tr, **opts)
 
     elapsed, per_call = time_calls(glm, torch, call, steps, warmup)
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    glm.forward(*args, w.k, scale, out=out, workspace=ws, topk_idx=idx, **opts)
+    fwd(*args, w.k, scale, out=out, workspace=ws, topk_idx=idx, **opts)
     counts = torch.bincount(idx.flatten().long(), minlength=w.E).cpu().numpy()
     return elapsed, per_call, counts
 
@@ -122,10 +124,11 @@ def record(w, elapsed, steps, per_call, counts, bound, traffic_kind=None):
     ms = elapsed * 1e3 / steps
     dom = max(("gate_up", "down", "shared_combine"), key=lambda s: per_call[s])
     t_dom = per_call[dom] * 1e-3
+    peak_mfma = PEAK_FP8_TFLOPS if w.dtype == "mxfp8" else PEAK_BF16_TFLOPS
     if bound == "mfma":
         ach = f[dom] / t_dom / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4),
                 "traffic": None, "work_per_launch": f[dom], "avg_launch_ms": round(per_call[dom], 4)}
         if dom == "gate_up" and traffic_kind:
             roof["traffic"] = measured_traffic(traffic_kind)
@@ -138,7 +141,7 @@ def record(w, elapsed, steps, per_call, counts, bound, traffic_kind=None):
             roof["traffic"] = measured_traffic(traffic_kind)
     t_layer = ms * 1e-3
     layer = {"tflops": round(lf / t_layer / 1e12, 2),
-             "frac_mfma": round(lf / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "frac_mfma": round(lf / t_layer / 1e12 / peak_mfma, 4),
              "hbm_gbs_algorithmic": round(lb / t_layer / 1e9, 1),
              "frac_hbm": round(lb / t_layer / 1e9 / PEAK_HBM_GBS, 4),
              "flops": lf, "bytes": lb}
@@ -269,6 +272,35 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
                                            args.warmup, dws, "hbm")
         log(f"dense decode: {res['dense_decode']['value']:,.0f} tokens/s")
     del dw, dws
+    torch.cuda.empty_cache()
+    # MXFP8 expert weights: the same draws encoded as MXFP8
+    res.update(mx_records(glm, torch, wl, args))
+    return res
+
+
+def mx_records(glm, torch, wl, args):
+    """The layer with MXFP8 expert weights at the prefill and decode sizes."""
+    from workloads.device import stream_layer, to_device
+    wp, wd = wl.WORKLOADS["glm_prefill_mx"], wl.WORKLOADS["glm_decode_mx"]
+    t0 = time.time()
+    dev, _ = stream_layer(wp)
+    log(f"MXFP8 layer weights resident ({time.time() - t0:.1f}s)")
+    n = max(glm.workspace_size(w.T, w.D, w.E, w.F, w.Fs, w.k, weight=glm.MXFP8) for w in (wp, wd))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    res = {}
+    for key, w, steps, bound in (("prefill_mxfp8", wp, args.steps, "mfma"),
+                                 ("decode_mxfp8", wd, args.decode_steps, "hbm")):
+        d = dev if w is wp else dev.with_x(to_device(wl.make_x(w)),
+                                           to_device(wl.make_corr_bias(w)), w)
+        e, pc, c = time_layer(glm, torch, d, w, steps, args.warmup, ws)
+        ms, roof, layer, load = record(w, e, steps, pc, c, bound)
+        res[key] = {"workload": w.name, "tokens": w.T, "value": round(w.T * steps / e, 1),
+                    "unit": "tokens/s", "steps": steps, "ms_per_step": round(ms, 4),
+                    "roofline": roof, "layer_roofline": layer, "routing_load": load,
+                    "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
+        log(f"{key}: {res[key]['value']:,.0f} tokens/s, stages {pc}")
+    del dev, ws
+    torch.cuda.empty_cache()
     return res
 
 
