@@ -83,19 +83,22 @@ def algorithmic(w, counts):
 
 
 def time_calls(glm, torch, call, steps, warmup):
-    """Run ``call(trace)`` warmup + steps times; wall time of the timed steps
-    (synchronised on both sides) and the per-call stage times from the HIP
-    events the library records on the call's stream."""
+    """Run ``call(trace)`` warmup + steps times untraced; wall time of the
+    timed steps (synchronised on both sides); then the same number of calls
+    with the library recording HIP events on the call's stream between its
+    stages, for the per-stage (per-kernel) times."""
     for _ in range(warmup):
         call(None)
     torch.cuda.synchronize()
-    tr = glm.Trace(max_calls=steps)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        call(None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tr = glm.Trace(max_calls=steps)
     for _ in range(steps):
         call(tr)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     stage_ms, n = tr.read()
     tr.close()
     return elapsed, {s: v / n for s, v in stage_ms.items()}

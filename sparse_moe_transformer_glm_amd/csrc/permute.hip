@@ -10,6 +10,35 @@ namespace {
 constexpr int kScanThreads = 1024;
 constexpr int kParts = kScanThreads / kMaxExperts;  // token-tile ranges scanned in parallel
 
+#ifndef GLM_BLK_M
+#define GLM_BLK_M 8
+#endif
+#ifndef GLM_BLK_N
+#define GLM_BLK_N 4
+#endif
+// Position `local` of a group's tile list -> (row tile m, column tile nt).
+// Routed groups (shared == false) hold few row tiles: column-tile major, row
+// tiles inner.  The shared (or dense) group's tiles all cost the same, so the
+// workgroups running together stay in step; they are listed in blocks of
+// GLM_BLK_M row tiles x GLM_BLK_N column tiles, so that the tiles running
+// together on one XCD read few distinct operand panels through its L2.
+__device__ inline void tile_order(int local, int mt, int nt_all, bool shared, int* m, int* nt) {
+  if (!shared) {
+    *nt = local / mt;
+    *m = local % mt;
+    return;
+  }
+  const int bm = min(GLM_BLK_M, mt), bn = GLM_BLK_N;
+  const int band = local / (bm * nt_all);          // band of bm row tiles
+  const int hb = min(bm, mt - band * bm);          // rows in this band
+  const int rem = local - band * bm * nt_all;
+  const int cb = rem / (hb * bn);                  // column block within the band
+  const int wb = min(bn, nt_all - cb * bn);        // columns in this block
+  const int r2 = rem - cb * hb * bn;
+  *m = band * bm + r2 % hb;
+  *nt = cb * bn + r2 / hb;
+}
+
 // Single workgroup.  masks[tile][e] has bit i set when token tile*64+i chose e.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const uint64_t* __restrict__ masks, ScanParams p, int32_t* __restrict__ counts,
@@ -36,36 +65,69 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   }
   part[q][e] = sum;
   __syncthreads();
+
+  // Per expert: count, then exclusive prefix sums of the counts and of the
+  // tile counts of both GEMMs over the 256 expert slots (a wave scan per 64
+  // experts, then the wave totals).
+  __shared__ int s_wsum[kMaxExperts / kWave][3];
+  int c = 0, v_gu = 0, v_dn = 0;
   if (tid < kMaxExperts) {
-    int c = 0;
 #pragma unroll
     for (int i = 0; i < kParts; ++i) c += part[i][tid];
     s_cnt[tid] = c;
+    if (tid < E) {
+      v_gu = cdiv(c, p.gu.BM) * (2 * p.F / p.gu.BN);
+      v_dn = cdiv(c, p.dn.BM) * (p.D / p.dn.BN);
+    } else {
+      c = 0;
+    }
+    const int lane = tid & (kWave - 1);
+    int i0 = c, i1 = v_gu, i2 = v_dn;  // inclusive sums within the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int a0 = __shfl_up(i0, d, kWave), a1 = __shfl_up(i1, d, kWave),
+                a2 = __shfl_up(i2, d, kWave);
+      if (lane >= d) { i0 += a0; i1 += a1; i2 += a2; }
+    }
+    if (lane == kWave - 1) {
+      s_wsum[tid / kWave][0] = i0;
+      s_wsum[tid / kWave][1] = i1;
+      s_wsum[tid / kWave][2] = i2;
+    }
+    // keep the exclusive values until the wave totals are known
+    c = i0 - c;
+    v_gu = i1 - v_gu;
+    v_dn = i2 - v_dn;
   }
   __syncthreads();
-
-  if (tid == 0) {
-    // expert offsets and the tile counts of each group of the two GEMMs
-    const int gu_nt = 2 * p.F / p.gu.BN, gu_nts = 2 * p.Fs / p.gu.BN;
-    const int dn_nt = p.D / p.dn.BN;
-    int off = 0, gu = 0, dn = 0;
-    for (int g = 0; g < E; ++g) {
-      const int c = s_cnt[g];
-      s_off[g] = off;
-      s_gu[g] = gu;
-      s_dn[g] = dn;
-      off += c;
-      gu += cdiv(c, p.gu.BM) * gu_nt;
-      dn += cdiv(c, p.dn.BM) * dn_nt;
+  if (tid < kMaxExperts) {
+    for (int w = 0; w < tid / kWave; ++w) {
+      c += s_wsum[w][0];
+      v_gu += s_wsum[w][1];
+      v_dn += s_wsum[w][2];
     }
-    s_off[E] = off;
+    if (tid <= E) {  // slot E holds the totals over the routed experts
+      s_off[tid] = c;
+      s_gu[tid] = v_gu;
+      s_dn[tid] = v_dn;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (E == kMaxExperts) {  // no slot E above: totals from the wave sums
+      int o = 0, gsum = 0, dsum = 0;
+      for (int w = 0; w < kMaxExperts / kWave; ++w) {
+        o += s_wsum[w][0];
+        gsum += s_wsum[w][1];
+        dsum += s_wsum[w][2];
+      }
+      s_off[E] = o;
+      s_gu[E] = gsum;
+      s_dn[E] = dsum;
+    }
     // the shared expert is group E of both GEMMs, over every token
-    s_gu[E] = gu;
-    gu += cdiv(p.T, p.gu.BM) * gu_nts;
-    s_gu[E + 1] = min(gu, p.gu_desc_cap);
-    s_dn[E] = dn;
-    dn += cdiv(p.T, p.dn.BM) * dn_nt;
-    s_dn[E + 1] = min(dn, p.dn_desc_cap);
+    s_gu[E + 1] = min(s_gu[E] + cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN), p.gu_desc_cap);
+    s_dn[E + 1] = min(s_dn[E] + cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN), p.dn_desc_cap);
   }
   __syncthreads();
 
@@ -97,8 +159,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int g = lo;
     const int rows = g < E ? s_cnt[g] : p.T;
     const int mt = cdiv(rows, p.gu.BM);
-    const int local = i - s_gu[g];
-    const int nt = local / mt, m = local % mt;
+    int nt, m;
+    tile_order(i - s_gu[g], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
     d.row0 = m * p.gu.BM;
@@ -116,8 +178,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int g = lo;
     const int grows = g < E ? s_cnt[g] : p.T;
     const int mt = cdiv(grows, p.dn.BM);
-    const int local = i - s_dn[g];
-    const int nt = local / mt, m = local % mt;
+    int nt, m;
+    tile_order(i - s_dn[g], mt, p.D / p.dn.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
     d.row0 = m * p.dn.BM;
