@@ -6,15 +6,26 @@
 namespace glm {
 namespace {
 
-// bf16 nearest-even of a double, rounded once: round to fp32 toward zero and
-// mark inexact results in the last bit (round to odd), then to bf16.  With 16
-// spare bits in fp32 the second rounding sees the true position relative to
-// the bf16 midpoint, so the result equals a direct rounding.  (Finite inputs.)
+// bf16 nearest-even of a double, rounded once.  Outside bf16's normal range:
+// round to fp32 toward zero and mark inexact results in the last bit (round
+// to odd), then to bf16; with 16 spare bits in fp32 the second rounding sees
+// the true position relative to the bf16 midpoint, so the result equals a
+// direct rounding.  (Finite inputs.)
 __device__ inline bf16_t f64_to_bf16(double v) {
+  // Values in bf16's normal range (all but zero and |v| < 2^-126 in
+  // practice): round the 63-bit exponent+mantissa pattern to 7 mantissa bits,
+  // nearest even, with the carry running into the exponent; then rebias.
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+  const uint32_t e = (uint32_t)(mag >> 52);
+  if (e > 1023 - 127 && e < 1023 + 127) {
+    const uint64_t r = (mag + 0xFFFFFFFFFFFull + ((mag >> 45) & 1ull)) >> 45;
+    return (bf16_t)((uint32_t)(r - ((uint64_t)(1023 - 127) << 7)) | (uint32_t)((u >> 48) & 0x8000u));
+  }
   const float f = __double2float_rz(v);
-  uint32_t u = __float_as_uint(f);
-  if ((double)f != v) u |= 1u;
-  return f32_to_bf16(__uint_as_float(u));
+  uint32_t w = __float_as_uint(f);
+  if ((double)f != v) w |= 1u;
+  return f32_to_bf16(__uint_as_float(w));
 }
 
 // xn[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w, one wave per row.
@@ -73,14 +84,77 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h
   }
 }
 
+// bf16 rows of up to NC * 2048 elements: one workgroup (4 waves) per row,
+// each lane holding NC 16-byte chunks in registers, so the row is read from
+// memory once.  The fp64 sum of squares is reduced in a fixed order (lane
+// chunks, wave butterfly, then the 4 wave sums in order), as deterministic as
+// rmsnorm_kernel, though associated differently.
+template <int NC>
+__global__ __launch_bounds__(256) void rmsnorm_bf16_row_kernel(const bf16_t* __restrict__ h,
+                                                              const float* __restrict__ w,
+                                                              bf16_t* __restrict__ out, int D,
+                                                              float eps) {
+  __shared__ double s_part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16_t* hr = h + (size_t)blockIdx.x * D;
+  uint4 v[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int d = (c * 256 + tid) * 8;
+    v[c] = d < D ? *reinterpret_cast<const uint4*>(hr + d) : make_uint4(0, 0, 0, 0);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t u[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double a = __uint_as_float(u[i] << 16), b = __uint_as_float(u[i] & 0xFFFF0000u);
+      ss = fma(a, a, ss);
+      ss = fma(b, b, ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  ss = ((s_part[0] + s_part[1]) + s_part[2]) + s_part[3];
+  const double r = 1.0 / sqrt(ss / (double)D + (double)eps);
+  bf16_t* o = out + (size_t)blockIdx.x * D;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int d = (c * 256 + tid) * 8;
+    if (d >= D) continue;
+    const float4 w0 = *reinterpret_cast<const float4*>(w + d);
+    const float4 w1 = *reinterpret_cast<const float4*>(w + d + 4);
+    const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint32_t u[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double a = (double)__uint_as_float(u[i] << 16) * r * (double)ww[2 * i];
+      const double b = (double)__uint_as_float(u[i] & 0xFFFF0000u) * r * (double)ww[2 * i + 1];
+      q[i] = (uint32_t)f64_to_bf16(a) | ((uint32_t)f64_to_bf16(b) << 16);
+    }
+    *reinterpret_cast<uint4*>(o + d) = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const void* h, const float* w, void* out, int T, int D, float eps,
                           bool bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const unsigned grid = (unsigned)cdiv(T, 4);
-  if (bf16) rmsnorm_kernel<true><<<grid, 256, 0, s>>>(h, w, out, T, D, eps);
-  else rmsnorm_kernel<false><<<grid, 256, 0, s>>>(h, w, out, T, D, eps);
+  const bf16_t* hb = static_cast<const bf16_t*>(h);
+  bf16_t* ob = static_cast<bf16_t*>(out);
+  const int chunks = cdiv(D, 2048);  // 16-byte chunks per lane of a 256-lane row
+  if (!bf16) rmsnorm_kernel<false><<<grid, 256, 0, s>>>(h, w, out, T, D, eps);
+  else if (chunks == 1) rmsnorm_bf16_row_kernel<1><<<T, 256, 0, s>>>(hb, w, ob, D, eps);
+  else if (chunks == 2) rmsnorm_bf16_row_kernel<2><<<T, 256, 0, s>>>(hb, w, ob, D, eps);
+  else if (chunks == 3) rmsnorm_bf16_row_kernel<3><<<T, 256, 0, s>>>(hb, w, ob, D, eps);
+  else if (chunks == 4) rmsnorm_bf16_row_kernel<4><<<T, 256, 0, s>>>(hb, w, ob, D, eps);
+  else rmsnorm_kernel<true><<<grid, 256, 0, s>>>(h, w, out, T, D, eps);
   return hipGetLastError();
 }
 

@@ -144,8 +144,14 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
     P.ksplit = cdiv(P.D, P.kchunk);
     const double per_group = dense ? (double)T : (double)A / P.E;
     const bool wide_gu = (dense || P.F % 128 == 0) && P.Fs % 128 == 0;
-    P.gu = mx ? gemm_shape_mx(per_group, wide_gu) : gemm_shape(per_group, wide_gu);
-    P.dn = mx ? gemm_shape_mx(per_group, P.D % 256 == 0) : gemm_shape(per_group, P.D % 256 == 0);
+    // A dense layer on a decode-size batch is a single group of a few rows:
+    // the 128 x 256 tiles would leave most CUs idle (144 tiles at width
+    // 18432, 24 in the down projection), the 32 x 64 tiles give 4x more.
+    const bool few_tiles = dense && per_group <= 96.0;
+    P.gu = mx ? gemm_shape_mx(per_group, wide_gu && !few_tiles)
+              : gemm_shape(per_group, wide_gu && !few_tiles);
+    P.dn = mx ? gemm_shape_mx(per_group, P.D % 256 == 0 && !few_tiles)
+              : gemm_shape(per_group, P.D % 256 == 0 && !few_tiles);
     // routed tiles, then the shared (or dense) group's tiles (group E)
     P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) +
                cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
