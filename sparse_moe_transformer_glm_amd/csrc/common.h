@@ -35,6 +35,8 @@ struct GemmShape {
 // ------------------------------------------------------- launch wrappers
 // Each returns hipGetLastError() after enqueueing on `s`.
 
+// Token rows per router-logits workgroup for a batch of T tokens.
+int router_tile_rows(int T);
 // Router logits.  partial[ks][T][E] fp32 = x[:, kslice] . router_w[:, kslice]^T.
 // Both also clear masks[ceil(T/64)][E] for the top-k kernel.
 hipError_t launch_router_logits_bf16(const bf16_t* x, const float* router_w, float* partial,

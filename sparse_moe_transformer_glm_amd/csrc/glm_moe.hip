@@ -134,7 +134,7 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
 
   if (bf16) {
     // enough (token tile, expert group, K slice) workgroups to cover the chip
-    const int base = cdiv(T, 64) * cdiv(P.E > 0 ? P.E : 1, 64);
+    const int base = cdiv(T, router_tile_rows(T)) * cdiv(P.E > 0 ? P.E : 1, 64);
     int ks = cdiv(512, base > 0 ? base : 1);
     const int ksteps = P.D / 64;
     if (ks > 24) ks = 24;

@@ -3,6 +3,8 @@
 // "GLM-5.2 model anatomy", Feed-forward / Mixture of Experts panel).
 #include "common.h"
 
+#include <type_traits>
+
 namespace glm {
 namespace {
 
@@ -35,57 +37,134 @@ __device__ inline void split3(const float4 w0, const float4 w1, bf16x8& hi, bf16
   lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
 }
 
-// One workgroup: 64 tokens x 64 experts over one K slice.  Wave w owns experts
-// [16w, 16w+16) of the group and all 64 tokens (four 16-row MFMA blocks).
+#ifndef GLM_ROUTER_MT
+#define GLM_ROUTER_MT 8  // 16-row token blocks per workgroup on large batches
+#endif
+#ifndef GLM_ROUTER_ST
+#define GLM_ROUTER_ST 2  // LDS stages of the large-batch tile
+#endif
+
+// One workgroup: MT*16 tokens x 64 experts over one K slice.  Wave w owns
+// experts [16w, 16w+16) and every token of the tile (MT 16-row MFMA blocks).
 // MFMA 16x16x32 bf16: lane l supplies row (l % 16), k-group (l / 16) of both
 // operands; the accumulator holds rows 4*(l/16)+r, column l % 16.
+//
+// K goes in steps of 64 through a ring of ST LDS stages filled by 16-byte
+// LDS-DMA loads: the x tile (bf16 rows of 128 B) and the fp32 router rows
+// (256 B) are read once per workgroup and shared by its four waves.  The
+// 16-byte chunks of every row are XOR-swizzled so that the 16 rows a
+// fragment read touches fall on distinct banks.  Each weight is split into
+// three bf16 terms right before its MFMAs (w = hi + mid + lo exactly).
+template <int MT, int ST>
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
     int T, int D, int E, int kchunk, uint64_t* __restrict__ masks, int n_masks) {
-  // clear the routing masks the top-k kernel fills (the grid has enough threads)
+  constexpr int XB = MT * 16 * 128;          // x tile bytes per stage
+  constexpr int WB = 64 * 256;               // router tile bytes per stage
+  constexpr int X_INST = XB / 1024, W_INST = WB / 1024;  // 1-KB DMA instructions
+  constexpr int IPW = (X_INST + W_INST) / 4;
+  static_assert((X_INST + W_INST) % 4 == 0, "every wave issues the same number of DMAs");
+  static_assert(ST == 2 || ST == 3, "ring of two or three stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[XB + WB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[XB + WB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[ST > 2 ? XB + WB : 16];
+
+  // clear the routing masks the top-k kernel fills
   {
+    const int nb = gridDim.x * gridDim.y * gridDim.z;
     const int b = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-    const int i = b * 256 + threadIdx.x;
-    if (i < n_masks) masks[i] = 0ull;
+    for (int i = b * 256 + threadIdx.x; i < n_masks; i += nb * 256) masks[i] = 0ull;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, kg = lane >> 4;
-  const int t0 = blockIdx.x * 64;
-  const int e0 = blockIdx.y * 64 + wave * 16;
+  const int t0 = blockIdx.x * (MT * 16);
+  const int e0 = blockIdx.y * 64;
   const int ks = blockIdx.z;
   const int kbeg = ks * kchunk;
-  const int kend = min(D, kbeg + kchunk);
+  const int nk = (min(D, kbeg + kchunk) - kbeg) / 64;
 
-  const float* wrow = W + (size_t)min(e0 + r16, E - 1) * D;
-  const bf16_t* xrow[4];
+  // DMA sources: instruction q = wave + 4i fills 1 KB of the stage; lane l
+  // writes physical chunk l % 8 of x row 8q + l/8, or physical chunk l % 16
+  // of router row 4(q - X_INST) + l/16.
+  const uint8_t* src[IPW];
+  int dst[IPW];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) xrow[m] = x + (size_t)min(t0 + 16 * m + r16, T - 1) * D;
-
-  f32x4 acc[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  for (int k = kbeg; k < kend; k += 32) {
-    const int kk = k + kg * 8;
-    const float4 w0 = *reinterpret_cast<const float4*>(wrow + kk);
-    const float4 w1 = *reinterpret_cast<const float4*>(wrow + kk + 4);
-    bf16x8 a[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const bf16x8*>(xrow[m] + kk);
-    bf16x8 hi, mid, lo;
-    split3(w0, w1, hi, mid, lo);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], lo, acc[m], 0, 0, 0);
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], mid, acc[m], 0, 0, 0);
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], hi, acc[m], 0, 0, 0);
+  for (int i = 0; i < IPW; ++i) {
+    const int q = wave + 4 * i;
+    if (q < X_INST) {
+      const int r = q * 8 + lane / 8;
+      const int lc = (lane % 8) ^ ((r >> 1) & 7);
+      src[i] = reinterpret_cast<const uint8_t*>(x + (size_t)min(t0 + r, T - 1) * D + kbeg + lc * 8);
+      dst[i] = q * 1024;
+    } else {
+      const int r = (q - X_INST) * 4 + lane / 16;
+      const int lc = (lane % 16) ^ (r & 15);
+      src[i] = reinterpret_cast<const uint8_t*>(W + (size_t)min(e0 + r, E - 1) * D + kbeg + lc * 4);
+      dst[i] = XB + (q - X_INST) * 1024;
     }
   }
+  auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? lds0 : s == 1 ? lds1 : lds2; };
+  auto issue = [&](uint8_t* st, int kt) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const size_t step = (wave + 4 * i < X_INST) ? (size_t)kt * 128 : (size_t)kt * 256;
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + step), (lds_void*)(st + dst[i]),
+                                       16, 0, 0);
+    }
+  };
 
-  const int e = e0 + r16;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int xsw = (r16 >> 1) & 7;  // swizzle of x rows 16m + r16
+  auto compute = [&](const uint8_t* st) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int xc = ((4 * sub + kg) ^ xsw) * 16;
+      const int wc0 = ((8 * sub + 2 * kg) ^ r16) * 16, wc1 = ((8 * sub + 2 * kg + 1) ^ r16) * 16;
+      const uint8_t* wrow = st + XB + (wave * 16 + r16) * 256;
+      const float4 w0 = *reinterpret_cast<const float4*>(wrow + wc0);
+      const float4 w1 = *reinterpret_cast<const float4*>(wrow + wc1);
+      bf16x8 a[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        a[m] = *reinterpret_cast<const bf16x8*>(st + (16 * m + r16) * 128 + xc);
+      bf16x8 hi, mid, lo;
+      split3(w0, w1, hi, mid, lo);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], lo, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], mid, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], hi, acc[m], 0, 0, 0);
+      }
+    }
+  };
+
+  // Step kt: wait for its stage (later stages may stay in flight), meet the
+  // barrier (every wave is then also done with the stage read at kt-1),
+  // refill that stage ST-1 steps ahead, compute.
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) issue(stage_ptr(s), s);
+  auto step = [&](auto sc, int kt) {
+    constexpr int s = decltype(sc)::value;
+    if (ST == 3 && kt + 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW));
+    else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+    lds_barrier();
+    if (kt + ST - 1 < nk) issue(stage_ptr((s + ST - 1) % ST), kt + ST - 1);
+    compute(stage_ptr(s));
+  };
+  for (int kt = 0; kt < nk; kt += ST) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (ST > 2) if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+  }
+
+  const int e = e0 + wave * 16 + r16;
   if (e >= E) return;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 16 * m + 4 * kg + r;
@@ -250,14 +329,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 
 }  // namespace
 
+int router_tile_rows(int T) { return T > 64 ? GLM_ROUTER_MT * 16 : 64; }
+
 hipError_t launch_router_logits_bf16(const bf16_t* x, const float* router_w, float* partial,
                                      int T, int D, int E, int ksplit, int kchunk,
                                      uint64_t* masks, hipStream_t s) {
-  dim3 grid(cdiv(T, 64), cdiv(E, 64), ksplit);
-  // masks: ceil(T/64) * E <= ceil(T/64) * 256 <= number of threads
+  const int rows = router_tile_rows(T);
+  dim3 grid(cdiv(T, rows), cdiv(E, 64), ksplit);
   const int n_masks = cdiv(T, kTokTile) * E;
-  router_logits_bf16_kernel<<<grid, 256, 0, s>>>(x, router_w, partial, T, D, E, kchunk, masks,
-                                                 n_masks);
+  if (rows == 64)
+    router_logits_bf16_kernel<4, 3><<<grid, 256, 0, s>>>(x, router_w, partial, T, D, E, kchunk,
+                                                         masks, n_masks);
+  else
+    router_logits_bf16_kernel<GLM_ROUTER_MT, GLM_ROUTER_ST><<<grid, 256, 0, s>>>(
+        x, router_w, partial, T, D, E, kchunk, masks, n_masks);
   return hipGetLastError();
 }
 
