@@ -220,11 +220,16 @@ GLM_MOE_API int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* 
 /* MXFP8 expert weights (OCP Microscaling v1.0 MXFP8): each tensor is E4M3
  * codes (1 byte; bias 7, max 448, no infinities) in the bf16 layout above, plus
  * one E8M0 scale byte (value 2^(s - 127)) per 32 consecutive elements along
- * its rows (the contraction dimension):
- *   w1, w3 [E][F][D] codes, w1_scale, w3_scale [E][F][D/32];
- *   w2 [E][D][F] codes, w2_scale [E][D][F/32];
- *   shared_w1, shared_w3 [F_shared][D], scales [F_shared][D/32];
- *   shared_w2 [D][F_shared], scale [D][F_shared/32].
+ * its rows (the contraction dimension).
+ *
+ * Scale layout ("K-step-major"): for a matrix of N rows and contraction K,
+ * the four scales of row n covering elements [128 kt, 128 kt + 128) form the
+ * dword at byte (kt * N + n) * 4, i.e. the array is [K/128][N][4] rather than
+ * the row-major [N][K/32]; glm_moe_mx_pack_scales converts.  Per tensor:
+ *   w1, w3 [E][F][D] codes, w1_scale, w3_scale [E][D/128][F][4];
+ *   w2 [E][D][F] codes, w2_scale [E][F/128][D][4];
+ *   shared_w1, shared_w3 [F_shared][D], scales [D/128][F_shared][4];
+ *   shared_w2 [D][F_shared], scale [F_shared/128][D][4].
  * The pages name FP8 GLM-5.2 artifacts (frontier-model-atlas "GLM-5.2 model
  * anatomy", release panel) without their scaling; this block format is the
  * one gfx950 applies inside its FP8 MFMA. */
@@ -254,6 +259,15 @@ GLM_MOE_API int glm_moe_forward_mx(const glm_moe_dims* d, const glm_moe_options*
                                    float* out, int32_t* topk_idx_out, float* topk_w_out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
                                    glm_moe_trace* trace);
+
+/* Reorder MX scales from row-major [n_mats][N][K/32] (src) to the
+ * K-step-major layout [n_mats][K/128][N][4] (dst) that glm_moe_forward_mx
+ * reads; a pure byte permutation, run on `stream`.  Both are device
+ * pointers, 16-byte aligned, of n_mats * N * K / 32 bytes each, and must not
+ * overlap.  K must be a positive multiple of 128 and N positive (EINVAL
+ * otherwise); n_mats == 0 does nothing.  For expert tensors pass n_mats = E. */
+GLM_MOE_API int glm_moe_mx_pack_scales(const void* src, void* dst, int64_t n_mats, int N, int K,
+                                       hipStream_t stream);
 
 /* Static text for a status code. */
 GLM_MOE_API const char* glm_moe_status_string(int status);

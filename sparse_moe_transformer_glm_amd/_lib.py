@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp, vp, sz, vp, vp]
         L.glm_moe_dense_workspace_size.argtypes = [pd, po, ctypes.POINTER(sz)]
         L.glm_moe_dense_ffn.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.glm_moe_mx_pack_scales.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
         L.glm_moe_trace_create.argtypes = [ctypes.POINTER(vp), i32]
         L.glm_moe_trace_destroy.argtypes = [vp]
         L.glm_moe_trace_reset.argtypes = [vp]
@@ -88,7 +89,7 @@ def lib() -> ctypes.CDLL:
                      "glm_moe_route_ex", "glm_moe_forward", "glm_moe_forward_traced",
                      "glm_moe_forward_ex", "glm_moe_forward_mx", "glm_moe_dense_workspace_size", "glm_moe_dense_ffn",
                      "glm_moe_trace_create", "glm_moe_trace_destroy", "glm_moe_trace_reset",
-                     "glm_moe_trace_read"):
+                     "glm_moe_trace_read", "glm_moe_mx_pack_scales"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -295,6 +296,22 @@ def dense_ffn(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Ten
     return out
 
 
+def pack_mx_scales(scales: torch.Tensor) -> torch.Tensor:
+    """Row-major MX scales [..., N, K/32] (uint8, on the GPU) -> the
+    K-step-major layout [..., K/128, N, 4] that ``forward_mx`` takes."""
+    if scales.dim() < 2:
+        raise ValueError("scales must be [..., N, K/32]")
+    *lead, N, KS = scales.shape
+    n_mats = 1
+    for v in lead:
+        n_mats *= v
+    out = torch.empty((*lead, KS // 4, N, 4), dtype=torch.uint8, device=scales.device)
+    st = lib().glm_moe_mx_pack_scales(_ptr(scales, "scales", torch.uint8), _ptr(out, "out"),
+                                      n_mats, N, KS * 32, _stream())
+    _check(st, "glm_moe_mx_pack_scales")
+    return out
+
+
 def forward_mx(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
                w1: torch.Tensor, w1_scale: torch.Tensor, w3: torch.Tensor,
                w3_scale: torch.Tensor, w2: torch.Tensor, w2_scale: torch.Tensor,
@@ -308,7 +325,8 @@ def forward_mx(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
                group_topk: int = 0, norm_weight: Optional[torch.Tensor] = None,
                norm_eps: float = 1e-5, residual: bool = False) -> torch.Tensor:
     """The layer with MXFP8 expert weights (uint8 E4M3 codes and uint8 E8M0
-    scales, one per 32 elements along each row); x is bfloat16."""
+    scales, one per 32 elements along each row, in the K-step-major layout of
+    ``pack_mx_scales``); x is bfloat16."""
     T, D = x.shape
     E, F, _ = w1.shape
     Fs = shared_w1.shape[0]
@@ -316,15 +334,15 @@ def forward_mx(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
     d = dims(T, D, E, F, Fs, x.dtype, MXFP8)
     o = options(n_group, topk_group, group_topk, norm_weight, norm_eps, residual, D)
     W = MxWeights(
-        _ptr(w1, "w1", u8, (E, F, D)), _ptr(w1_scale, "w1_scale", u8, (E, F, D // 32)),
-        _ptr(w3, "w3", u8, (E, F, D)), _ptr(w3_scale, "w3_scale", u8, (E, F, D // 32)),
-        _ptr(w2, "w2", u8, (E, D, F)), _ptr(w2_scale, "w2_scale", u8, (E, D, F // 32)),
+        _ptr(w1, "w1", u8, (E, F, D)), _ptr(w1_scale, "w1_scale", u8, (E, D // 128, F, 4)),
+        _ptr(w3, "w3", u8, (E, F, D)), _ptr(w3_scale, "w3_scale", u8, (E, D // 128, F, 4)),
+        _ptr(w2, "w2", u8, (E, D, F)), _ptr(w2_scale, "w2_scale", u8, (E, F // 128, D, 4)),
         _ptr(shared_w1, "shared_w1", u8, (Fs, D)),
-        _ptr(shared_w1_scale, "shared_w1_scale", u8, (Fs, D // 32)),
+        _ptr(shared_w1_scale, "shared_w1_scale", u8, (D // 128, Fs, 4)),
         _ptr(shared_w3, "shared_w3", u8, (Fs, D)),
-        _ptr(shared_w3_scale, "shared_w3_scale", u8, (Fs, D // 32)),
+        _ptr(shared_w3_scale, "shared_w3_scale", u8, (D // 128, Fs, 4)),
         _ptr(shared_w2, "shared_w2", u8, (D, Fs)),
-        _ptr(shared_w2_scale, "shared_w2_scale", u8, (D, Fs // 32)))
+        _ptr(shared_w2_scale, "shared_w2_scale", u8, (Fs // 128, D, 4)))
     if out is None:
         out = torch.empty((T, D), dtype=torch.float32, device=x.device)
     if workspace is None:

@@ -123,17 +123,18 @@ hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, const
 // along the contraction dimension; scale arrays are [rows][K/32] bytes).
 struct MxGateUpArgs {
   const uint8_t* xq;           // [T][D]   layer input, quantised per token
-  const uint8_t* xs;           // [T][D/32]
+  const uint8_t* xs;           // [D/128][T][4] (scales K-step-major)
+  const uint8_t* xsp;          // [D/128][T*k][4]: the same scales in expert-row order
   const int32_t* row_assign;
   const int32_t* offsets;
-  const uint8_t* w1; const uint8_t* w1s;   // [E][F][D], [E][F][D/32]
+  const uint8_t* w1; const uint8_t* w1s;   // [E][F][D], [E][D/128][F][4]
   const uint8_t* w3; const uint8_t* w3s;
-  const uint8_t* sw1; const uint8_t* sw1s; // [Fs][D], [Fs][D/32]
+  const uint8_t* sw1; const uint8_t* sw1s; // [Fs][D], [D/128][Fs][4]
   const uint8_t* sw3; const uint8_t* sw3s;
   const TileDesc* desc;
   const int32_t* desc_count;
-  uint8_t* H; uint8_t* Hsc;    // [T*k][F], [T*k][F/32]: gated hidden rows, quantised
-  uint8_t* Hs; uint8_t* Hssc;  // [T][Fs], [T][Fs/32]
+  uint8_t* H; uint8_t* Hsc;    // [T*k][F], [F/128][T*k][4]: gated hidden rows, quantised
+  uint8_t* Hs; uint8_t* Hssc;  // [T][Fs], [Fs/128][T][4]
   int T, D, E, F, Fs, k;
   int grid;
 };
@@ -142,8 +143,8 @@ struct MxDownArgs {
   const uint8_t* Hs; const uint8_t* Hssc;
   const int32_t* row_assign;
   const int32_t* offsets;
-  const uint8_t* w2; const uint8_t* w2s;   // [E][D][F], [E][D][F/32]
-  const uint8_t* sw2; const uint8_t* sw2s; // [D][Fs], [D][Fs/32]
+  const uint8_t* w2; const uint8_t* w2s;   // [E][D][F], [E][F/128][D][4]
+  const uint8_t* sw2; const uint8_t* sw2s; // [D][Fs], [Fs/128][D][4]
   const float* topk_w;
   const TileDesc* desc;
   const int32_t* desc_count;
@@ -151,9 +152,16 @@ struct MxDownArgs {
   int T, D, E, F, Fs, k;
   int grid;
 };
-// x (bf16 [T][D]) -> MXFP8 codes [T][D] and scales [T][D/32].
+// x (bf16 [T][D]) -> MXFP8 codes [T][D] and K-step-major scales [D/128][T][4].
 hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int T, int D,
                               hipStream_t s);
+// Input scales in expert-row order: xsp[kt][row] = xs[kt][row_assign[row] / k]
+// (dwords), so a tile's routed rows read contiguous scales.
+hipError_t launch_permute_mx_scales(const uint8_t* xs, const int32_t* row_assign, int T, int k,
+                                    int D, uint8_t* xsp, hipStream_t s);
+// Row-major MX scales [n_mats][N][K/32] -> K-step-major [n_mats][K/128][N][4].
+hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, size_t n_mats, int N, int K,
+                                 hipStream_t s);
 // Tile shape of an MXFP8 grouped GEMM launch (same `wide` rule as gemm_shape).
 GemmShape gemm_shape_mx(double rows_per_group, bool wide);
 hipError_t launch_gateup_mx(const MxGateUpArgs& a, GemmShape sh, hipStream_t s);

@@ -12,6 +12,13 @@
 // stages filled by 16-byte LDS-DMA loads.  Each stage also holds the tile's
 // E8M0 scales for the step (4 per row, one dword), loaded by 4-byte LDS-DMA.
 //
+// Scales are stored K-step-major: the four scales of row n for K step kt
+// (elements [128kt, 128kt+128)) are the dword at (kt * N + n) * 4 of the
+// matrix's scale array (N rows), so the 64 rows of one scale copy are 256
+// contiguous bytes.  The weights arrive in this layout (the pack entry point
+// converts from row-major scales); the quantised activations and hidden rows
+// are written in it.
+//
 // MFMA operand layout (checked on gfx950): lane l supplies row l % 32; with
 // g = l / 32 its 32 bytes are K elements [16g, 16g+16) and [32+16g, 32+16g+16)
 // of the 64-element step, and the scale it passes covers K elements
@@ -136,41 +143,54 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   }
   const int KS = K / 32;  // scale bytes per row
 
-  // data and scale rows of A (tile row rr) and B (tile column n)
-  auto a_row = [&](int rr, const uint8_t** data, const uint8_t** sc) {
+  // Data row and K-step-0 scale dword of A (tile row rr) and B (tile column
+  // n); *sstep is the byte distance between K steps of that scale array.
+  auto a_row = [&](int rr, const uint8_t** data, const uint8_t** sc, size_t* sstep) {
     rr = min(rr, rows - 1);  // rows past the tile repeat its last row
     if constexpr (MODE == GATE_UP) {
-      const int tok = (g == gu.E) ? row0 + rr
-                                  : gu.row_assign[gu.offsets[g] + row0 + rr] / gu.k;
-      *data = gu.xq + (size_t)tok * K;
-      *sc = gu.xs + (size_t)tok * KS;
+      if (g == gu.E) {
+        *data = gu.xq + (size_t)(row0 + rr) * K;
+        *sc = gu.xs + (size_t)(row0 + rr) * 4;
+        *sstep = (size_t)gu.T * 4;
+      } else {
+        const int r = gu.offsets[g] + row0 + rr;
+        *data = gu.xq + (size_t)(gu.row_assign[r] / gu.k) * K;
+        *sc = gu.xsp + (size_t)r * 4;
+        *sstep = (size_t)gu.T * gu.k * 4;
+      }
     } else if (g == dn.E) {
       *data = dn.Hs + (size_t)(row0 + rr) * K;
-      *sc = dn.Hssc + (size_t)(row0 + rr) * KS;
+      *sc = dn.Hssc + (size_t)(row0 + rr) * 4;
+      *sstep = (size_t)dn.T * 4;
     } else {
       const size_t r = (size_t)(dn.offsets[g] + row0 + rr);
       *data = dn.H + r * K;
-      *sc = dn.Hsc + r * KS;
+      *sc = dn.Hsc + r * 4;
+      *sstep = (size_t)dn.T * dn.k * 4;
     }
   };
-  auto b_row = [&](int n, const uint8_t** data, const uint8_t** sc) {
+  auto b_row = [&](int n, const uint8_t** data, const uint8_t** sc, size_t* sstep) {
     if constexpr (MODE == GATE_UP) {
       const int blk = n / 32, hcol = col0 + (blk / 2) * 32 + (n % 32);
       const bool up = blk & 1;
-      size_t r;
       if (g == gu.E) {
-        r = (size_t)hcol;
-        *data = (up ? gu.sw3 : gu.sw1) + r * K;
-        *sc = (up ? gu.sw3s : gu.sw1s) + r * KS;
+        *data = (up ? gu.sw3 : gu.sw1) + (size_t)hcol * K;
+        *sc = (up ? gu.sw3s : gu.sw1s) + (size_t)hcol * 4;
+        *sstep = (size_t)gu.Fs * 4;
       } else {
-        r = (size_t)g * gu.F + hcol;
+        const size_t r = (size_t)g * gu.F + hcol;
         *data = (up ? gu.w3 : gu.w1) + r * K;
-        *sc = (up ? gu.w3s : gu.w1s) + r * KS;
+        *sc = (up ? gu.w3s : gu.w1s) + (size_t)g * gu.F * KS + (size_t)hcol * 4;
+        *sstep = (size_t)gu.F * 4;
       }
+    } else if (g == dn.E) {
+      *data = dn.sw2 + (size_t)(col0 + n) * K;
+      *sc = dn.sw2s + (size_t)(col0 + n) * 4;
+      *sstep = (size_t)dn.D * 4;
     } else {
-      const size_t r = (g == dn.E) ? (size_t)(col0 + n) : (size_t)g * dn.D + col0 + n;
-      *data = ((g == dn.E) ? dn.sw2 : dn.w2) + r * K;
-      *sc = ((g == dn.E) ? dn.sw2s : dn.w2s) + r * KS;
+      *data = dn.w2 + ((size_t)g * dn.D + col0 + n) * K;
+      *sc = dn.w2s + (size_t)g * dn.D * KS + (size_t)(col0 + n) * 4;
+      *sstep = (size_t)dn.D * 4;
     }
   };
 
@@ -184,28 +204,28 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     const int ch = (lane % CPR) ^ swz(r);
     const uint8_t* d;
     const uint8_t* sc;
-    if (r < BM) a_row(r, &d, &sc);
-    else b_row(r - BM, &d, &sc);
+    size_t step;
+    if (r < BM) a_row(r, &d, &sc, &step);
+    else b_row(r - BM, &d, &sc, &step);
     src[i] = d + ch * 16;
   }
   // Scale instruction j covers 64 rows: j < SA_INST the A rows, else B rows.
   // Waves beyond the instruction count repeat instruction j % S_INST (the
   // same bytes to the same place).
   const uint8_t* ssrc[SPW];
+  size_t sstep[SPW];
   int sdst[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int j = (wave + i * NW) % C::S_INST;
     const uint8_t* d;
-    const uint8_t* sc;
     if (j < C::SA_INST) {
-      a_row(j * 64 + lane, &d, &sc);
+      a_row(j * 64 + lane, &d, &ssrc[i], &sstep[i]);
       sdst[i] = C::SC_A + j * 256;
     } else {
-      b_row((j - C::SA_INST) * 64 + lane, &d, &sc);
+      b_row((j - C::SA_INST) * 64 + lane, &d, &ssrc[i], &sstep[i]);
       sdst[i] = C::SC_B + (j - C::SA_INST) * 256;
     }
-    ssrc[i] = sc;
   }
 
   if constexpr (MODE == DOWN) {
@@ -235,7 +255,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ssrc[i] + (size_t)kt * 4),
+      __builtin_amdgcn_global_load_lds((const void*)(ssrc[i] + (size_t)kt * sstep[i]),
                                        (lds_void*)(st + sdst[i]), 4, 0, 0);
   };
   constexpr int VPS = IPW + SPW;  // DMA instructions per wave per stage
@@ -352,7 +372,9 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     const int F = shared ? gu.Fs : gu.F;
     const size_t hrow0 = shared ? (size_t)row0 : (size_t)(gu.offsets[g] + row0);
     uint8_t* Hq = (shared ? gu.Hs : gu.H) + hrow0 * F;
-    uint8_t* Hsc = (shared ? gu.Hssc : gu.Hsc) + hrow0 * (F / 32);
+    // K-step-major scales over all rows of H (T * k) or Hs (T)
+    const size_t hrows = shared ? (size_t)gu.T : (size_t)gu.T * gu.k;
+    uint8_t* Hsc = (shared ? gu.Hssc : gu.Hsc) + hrow0 * 4;
 #pragma unroll
     for (int m = 0; m < FM; ++m) {
       if (m >= live_m) continue;  // uniform across the wave
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
           const int row = row_of(m, r);
           if (row < rows) {
             Hq[(size_t)row * F + hcol] = (uint8_t)code;
-            if (lr == 0) Hsc[(size_t)row * (F / 32) + hblk] = (uint8_t)(s + 127);
+            if (lr == 0) Hsc[((size_t)(hblk / 4) * hrows + row) * 4 + hblk % 4] = (uint8_t)(s + 127);
           }
         }
       }
@@ -395,12 +417,14 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   }
 }
 
-// One thread per 32-element block of x: block maximum, scale, codes.
+// One thread per 32-element block of x: block maximum, scale, codes.  The
+// scale goes to the K-step-major array [D/128][T][4].
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restrict__ x,
                                                           uint8_t* __restrict__ xq,
-                                                          uint8_t* __restrict__ xs, size_t nblk) {
+                                                          uint8_t* __restrict__ xs, int T,
+                                                          int nb) {
   const size_t b = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblk) return;
+  if (b >= (size_t)T * nb) return;
   const uint4* p = reinterpret_cast<const uint4*>(x + b * 32);
   uint32_t u[16];
 #pragma unroll
@@ -427,7 +451,35 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restri
   uint4* q = reinterpret_cast<uint4*>(xq + b * 32);
   q[0] = make_uint4(c[0], c[1], c[2], c[3]);
   q[1] = make_uint4(c[4], c[5], c[6], c[7]);
-  xs[b] = (uint8_t)(s + 127);
+  const int t = (int)(b / nb), j = (int)(b % nb);
+  xs[((size_t)(j / 4) * T + t) * 4 + j % 4] = (uint8_t)(s + 127);
+}
+
+// Input scales into expert-row order, one thread per output dword.
+__global__ __launch_bounds__(256) void permute_scales_kernel(const uint32_t* __restrict__ xs,
+                                                             const int32_t* __restrict__ row_assign,
+                                                             int T, int k, size_t rows, size_t n_dw,
+                                                             uint32_t* __restrict__ xsp) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_dw) return;
+  const size_t kt = i / rows, r = i % rows;
+  xsp[i] = xs[kt * T + row_assign[r] / k];
+}
+
+// Row-major scales [n_mats][N][K/32] -> K-step-major [n_mats][K/128][N][4]:
+// one thread per output dword (four consecutive scales of one row).
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ src,
+                                                          uint8_t* __restrict__ dst,
+                                                          size_t n_dw, int N, int ksteps) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_dw) return;
+  const size_t per = (size_t)N * ksteps;  // dwords per matrix
+  const size_t m = i / per;
+  const int r = (int)(i % per);
+  const int kt = r / N, n = r % N;
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(src + (m * N + n) * (size_t)ksteps * 4 +
+                                                        (size_t)kt * 4);
+  reinterpret_cast<uint32_t*>(dst)[i] = v;
 }
 
 // Tile configurations <BM, BN, WM, WN, stages>.  The prefill tile is
@@ -476,7 +528,27 @@ hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int T, 
                               hipStream_t s) {
   const size_t nblk = (size_t)T * (D / 32);
   if (nblk == 0) return hipSuccess;
-  gemm_mx::quantize_mx_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, s>>>(x, xq, xs, nblk);
+  gemm_mx::quantize_mx_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, s>>>(x, xq, xs, T,
+                                                                             D / 32);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_mx_scales(const uint8_t* xs, const int32_t* row_assign, int T, int k,
+                                    int D, uint8_t* xsp, hipStream_t s) {
+  const size_t rows = (size_t)T * k, n_dw = rows * (D / 128);
+  if (n_dw == 0) return hipSuccess;
+  gemm_mx::permute_scales_kernel<<<(unsigned)((n_dw + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const uint32_t*>(xs), row_assign, T, k, rows, n_dw,
+      reinterpret_cast<uint32_t*>(xsp));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, size_t n_mats, int N, int K,
+                                 hipStream_t s) {
+  const size_t n_dw = n_mats * (size_t)N * (K / 128);
+  if (n_dw == 0) return hipSuccess;
+  gemm_mx::pack_scales_kernel<<<(unsigned)((n_dw + 255) / 256), 256, 0, s>>>(src, dst, n_dw, N,
+                                                                             K / 128);
   return hipGetLastError();
 }
 

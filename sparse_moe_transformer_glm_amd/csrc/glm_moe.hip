@@ -43,7 +43,7 @@ struct Plan {
   float norm_eps;
   bool add_residual;
   size_t xnorm, partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
-      dn_desc, row_assign, H, Hs, Y, xq, xs, Hsc, Hssc;
+      dn_desc, row_assign, H, Hs, Y, xq, xs, xsp, Hsc, Hssc;
   size_t total;
 };
 
@@ -185,6 +185,7 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   P.Y = take((size_t)T * (P.k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
   P.xq = take(mx ? (size_t)T * P.D : 0);        // MXFP8 input codes and scales
   P.xs = take(mx ? (size_t)T * P.D / 32 : 0);
+  P.xsp = take(mx ? (size_t)A * P.D / 32 : 0);  // input scales in expert-row order
   P.Hsc = take(mx ? (size_t)A * P.F / 32 : 0);  // MXFP8 hidden-row scales
   P.Hssc = take(mx ? (size_t)T * P.Fs / 32 : 0);
   P.total = T == 0 ? 0 : o;
@@ -313,9 +314,11 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     uint8_t* xq = at<uint8_t>(ws, P.xq);
     uint8_t* xs = at<uint8_t>(ws, P.xs);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
+    uint8_t* xsp = at<uint8_t>(ws, P.xsp);
     GLM_HIP(launch_quantize_mx(static_cast<const bf16_t*>(xin), xq, xs, P.T, P.D, s));
+    GLM_HIP(launch_permute_mx_scales(xs, row_assign, P.T, P.k, P.D, xsp, s));
     MxGateUpArgs ga{};
-    ga.xq = xq; ga.xs = xs;
+    ga.xq = xq; ga.xs = xs; ga.xsp = xsp;
     ga.row_assign = row_assign; ga.offsets = offsets;
     ga.w1 = static_cast<const uint8_t*>(w1); ga.w1s = W.w1s;
     ga.w3 = static_cast<const uint8_t*>(w3); ga.w3s = W.w3s;
@@ -524,6 +527,22 @@ int glm_moe_forward_mx(const glm_moe_dims* d, const glm_moe_options* opts, const
                    workspace, stream, trace);
 }
 
+int glm_moe_mx_pack_scales(const void* src, void* dst, int64_t n_mats, int N, int K,
+                           hipStream_t stream) {
+  if (n_mats < 0 || N <= 0 || K <= 0 || K % 128)
+    return fail(GLM_MOE_EINVAL, "bad sizes n_mats=%lld N=%d K=%d (K a multiple of 128)",
+                (long long)n_mats, N, K);
+  if (n_mats == 0) return GLM_MOE_OK;
+  int st;
+  if ((st = check_ptr(src, "src")) || (st = check_ptr(dst, "dst"))) return st;
+  const size_t bytes = (size_t)n_mats * N * (K / 32);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(GLM_MOE_EINVAL, "src and dst overlap");
+  GLM_HIP(launch_pack_mx_scales(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst),
+                                (size_t)n_mats, N, K, stream));
+  return GLM_MOE_OK;
+}
+
 int glm_moe_forward_traced(const glm_moe_dims* d, const void* x, const float* router_w,
                            const float* corr_bias, const void* w1, const void* w3,
                            const void* w2, const void* shared_w1, const void* shared_w3,
@@ -642,6 +661,6 @@ const char* glm_moe_status_string(int status) {
 
 const char* glm_moe_last_error(void) { return g_err; }
 
-int glm_moe_version(void) { return 200; }
+int glm_moe_version(void) { return 300; }
 
 }  // extern "C"

@@ -353,3 +353,16 @@ def test_forward_mx_argument_checks():
                                      FAKE, 1 << 40, None) == glm.EINVAL
     # zero tokens: no-op
     assert _forward_mx(_mx_dims(T=0), None, x=0, out=0) == glm.OK
+
+
+def test_mx_pack_scales_argument_checks():
+    pack = glm.lib().glm_moe_mx_pack_scales
+    other = FAKE + (1 << 30)
+    assert pack(FAKE, other, 2, 64, 100, None) == glm.EINVAL          # K not a multiple of 128
+    assert pack(FAKE, other, 2, 0, 128, None) == glm.EINVAL           # no rows
+    assert pack(FAKE, other, -1, 64, 128, None) == glm.EINVAL
+    assert pack(0, other, 2, 64, 128, None) == glm.EINVAL             # null source
+    assert pack(FAKE, 0, 2, 64, 128, None) == glm.EINVAL
+    assert pack(FAKE + 4, other, 2, 64, 128, None) == glm.EINVAL      # misaligned
+    assert pack(FAKE, FAKE + 16, 2, 64, 128, None) == glm.EINVAL      # overlapping
+    assert pack(0, 0, 0, 64, 128, None) == glm.OK                     # nothing to do

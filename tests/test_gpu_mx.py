@@ -99,6 +99,22 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("shape", [(3, 70, 12), (130, 4), (2, 2, 256, 192)])
+def test_pack_scales_is_the_kstep_major_permutation(shape):
+    """glm_moe_mx_pack_scales against the permutation written out in NumPy:
+    byte (kt*N + n)*4 + j of each matrix = row-major scale [n][4kt + j]."""
+    rng = np.random.default_rng(sum(shape))
+    src = rng.integers(0, 256, shape, dtype=np.uint8)
+    *lead, N, KS = shape
+    want = np.empty((*lead, KS // 4, N, 4), np.uint8)
+    for kt in range(KS // 4):
+        for j in range(4):
+            want[..., kt, :, j] = src[..., :, 4 * kt + j]
+    got = glm.pack_mx_scales(torch.from_numpy(src).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_mx_layer_parity(name):
     w = CASES[name]

@@ -80,3 +80,19 @@ def test_mxfp8_layer_shapes():
     assert L.x.dtype == np.uint16
     (c, s), _, _ = L.expert(1)
     assert c.shape == (w.F, w.D) and s.shape == (w.F, w.D // 32)
+
+
+def test_kstep_major_marshalling_is_the_documented_permutation():
+    """The upload hands MX scales over as [..., K/128, N, 4]: byte j of dword
+    (kt, n) is the row-major scale [n][4kt + j]."""
+    import torch
+    from workloads.device import kstep_major
+    rng = np.random.default_rng(7)
+    src = rng.integers(0, 256, (3, 5, 16), dtype=np.uint8)
+    got = kstep_major(torch.from_numpy(src)).numpy()
+    assert got.shape == (3, 4, 5, 4)
+    for m in range(3):
+        for kt in range(4):
+            for n in range(5):
+                for j in range(4):
+                    assert got[m, kt, n, j] == src[m, n, 4 * kt + j]

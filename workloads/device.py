@@ -1,7 +1,9 @@
 """Upload seeded layer inputs to the GPU with PyTorch (memory plumbing only).
 
 Used by the GPU tests and the benchmark.  bf16 bit patterns (uint16) become
-``torch.bfloat16`` tensors with identical bits.
+``torch.bfloat16`` tensors with identical bits; MXFP8 scales, generated
+row-major [..., N, K/32], are handed over in the K-step-major layout
+[..., K/128, N, 4] the layer takes (a byte permutation).
 """
 from __future__ import annotations
 
@@ -19,6 +21,14 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(a).to(device)
+
+
+def kstep_major(scales: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """Row-major MX scales [..., N, K/32] -> [..., K/128, N, 4]."""
+    if scales is None:
+        return None
+    *lead, n, ks = scales.shape
+    return scales.reshape(*lead, n, ks // 4, 4).transpose(-3, -2).contiguous()
 
 
 def torch_dtype(w: Workload) -> torch.dtype:
@@ -63,9 +73,10 @@ class DeviceLayer:
 
 def upload_layer(L: HostLayer, device="cuda") -> DeviceLayer:
     t = lambda a: None if a is None else to_device(a, device)
+    s = lambda a: kstep_major(t(a))
     return DeviceLayer(L.w, t(L.x), t(L.router_w), t(L.corr_bias), t(L.w1), t(L.w3), t(L.w2),
-                       t(L.sw1), t(L.sw3), t(L.sw2), t(L.w1s), t(L.w3s), t(L.w2s), t(L.sw1s),
-                       t(L.sw3s), t(L.sw2s))
+                       t(L.sw1), t(L.sw3), t(L.sw2), s(L.w1s), s(L.w3s), s(L.w2s), s(L.sw1s),
+                       s(L.sw3s), s(L.sw2s))
 
 
 def stream_layer(w: Workload, device="cuda", keep_host: bool = False,
@@ -103,9 +114,10 @@ def stream_layer(w: Workload, device="cuda", keep_host: bool = False,
         sw1, sw3, sw2 = sh
         sc = [None, None, None]
     t = lambda a: None if a is None else to_device(a, device)
+    s = lambda a: kstep_major(t(a))
     dev = DeviceLayer(w, t(x), t(rw), t(cb), dev_t["w1"], dev_t["w3"], dev_t["w2"], t(sw1),
-                      t(sw3), t(sw2), dev_t.get("w1s"), dev_t.get("w3s"), dev_t.get("w2s"),
-                      t(sc[0]), t(sc[1]), t(sc[2]))
+                      t(sw3), t(sw2), kstep_major(dev_t.get("w1s")), kstep_major(dev_t.get("w3s")),
+                      kstep_major(dev_t.get("w2s")), s(sc[0]), s(sc[1]), s(sc[2]))
     host = None
     if keep_host:
         host = HostLayer(w, x, rw, cb, host_t["w1"], host_t["w3"], host_t["w2"], sw1, sw3, sw2,
