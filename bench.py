@@ -104,6 +104,39 @@ def time_calls(glm, torch, call, steps, warmup):
     return elapsed, {s: v / n for s, v in stage_ms.items()}
 
 
+def call_percentiles(torch, call, n):
+    """p10 / median / p90 of single-call times (HIP events on the launch
+    stream, one pair per call), from n more calls."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        call(None)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"p10": round(float(np.percentile(t, 10)), 4),
+            "p50": round(float(np.median(t)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4)}
+
+
+def time_route(glm, torch, dev, w, steps, warmup, ws):
+    """glm_moe_route alone (router logits, top-k, weights): ms per call."""
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        glm.route(dev.x, dev.router_w, dev.corr_bias, w.k, w.scale, workspace=ws,
+                  topk_idx=idx, topk_w=wt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        glm.route(dev.x, dev.router_w, dev.corr_bias, w.k, w.scale, workspace=ws,
+                  topk_idx=idx, topk_w=wt)
+    torch.cuda.synchronize()
+    return round((time.perf_counter() - t0) * 1e3 / steps, 4)
+
+
 def time_layer(glm, torch, dev, w, steps, warmup, ws, **opts):
     out = torch.empty((w.T, w.D), dtype=torch.float32, device="cuda")
     args = dev.args()
@@ -116,10 +149,15 @@ def time_layer(glm, torch, dev, w, steps, warmup, ws, **opts):
         fwd(*args, w.k, scale, out=out, workspace=ws, trace=tr, **opts)
 
     elapsed, per_call = time_calls(glm, torch, call, steps, warmup)
+    per_call["_pct"] = call_percentiles(torch, call, steps)
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
     fwd(*args, w.k, scale, out=out, workspace=ws, topk_idx=idx, **opts)
     counts = torch.bincount(idx.flatten().long(), minlength=w.E).cpu().numpy()
     return elapsed, per_call, counts
+
+
+def stages(per_call):
+    return {s: round(v, 4) for s, v in per_call.items() if not s.startswith("_")}
 
 
 def record(w, elapsed, steps, per_call, counts, bound, traffic_kind=None):
@@ -237,8 +275,8 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
                           "achieved": round(nb / (pc["norm"] * 1e-3) / 1e9, 1),
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": round(nb / (pc["norm"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
-    log(f"prefill block: {res['prefill_block']['value']:,.0f} tokens/s, stages {pc}")
+        "stages_ms": stages(pc)}
+    log(f"prefill block: {res['prefill_block']['value']:,.0f} tokens/s, stages {stages(pc)}")
     del h
     # group-limited routing (8 groups of 32, 4 kept) at scale 1.0
     e, pc, c = time_layer(glm, torch, dev, wp, args.steps, args.warmup, ws, n_group=8,
@@ -247,9 +285,9 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
         "what": "n_group 8, topk_group 4, group_topk 2, scale 1.0",
         "value": round(wp.T * args.steps / e, 1), "unit": "tokens/s",
         "ms_per_step": round(e * 1e3 / args.steps, 4),
-        "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
+        "stages_ms": stages(pc)}
     log(f"prefill group routing: {res['prefill_group_routing']['value']:,.0f} tokens/s, "
-        f"stages {pc}")
+        f"stages {stages(pc)}")
     if wd:
         dd = type(dev)(wd, to_device(wl.make_x(wd)), dev.router_w,
                        to_device(wl.make_corr_bias(wd)), dev.w1, dev.w3, dev.w2, dev.sw1,
@@ -259,7 +297,24 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
         res["decode_group_routing"] = {
             "value": round(wd.T * args.decode_steps / e, 1), "unit": "tokens/s",
             "ms_per_step": round(e * 1e3 / args.decode_steps, 4),
-            "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
+            "stages_ms": stages(pc)}
+    # skewed routing at the GLM shape: +1.5 on 16 hot experts (every assignment
+    # lands on them: MFMA-bound), and +0.2 (about 40% hot: weight streaming)
+    for key, name, bound in (("skew_literal", "glm_skew", "mfma"),
+                             ("skew_mild", "glm_skew_mild", "hbm")):
+        w = wl.WORKLOADS[name]
+        d = dev.with_x(to_device(wl.make_x(w)), to_device(wl.make_corr_bias(w)), w)
+        e, pc, c = time_layer(glm, torch, d, w, args.steps, args.warmup, ws)
+        ms, roof, layer, load = record(w, e, args.steps, pc, c, bound)
+        res[key] = {"workload": name, "tokens": w.T, "hot_bias": w.hot_value,
+                    "value": round(w.T * args.steps / e, 1), "unit": "tokens/s",
+                    "ms_per_step": round(ms, 4), "roofline": roof, "layer_roofline": layer,
+                    "routing_load": load, "hot_share": round(float(c[:w.hot_count].sum()) /
+                                                             float(c.sum()), 4),
+                    "stages_ms": stages(pc), "call_ms": pc["_pct"]}
+        log(f"{key}: {res[key]['value']:,.0f} tokens/s, hot share {res[key]['hot_share']}, "
+            f"stages {stages(pc)}")
+        del d
     # dense FFN of the leading dense layers (width: see workloads.GLM_DENSE_WIDTH)
     F = wl.GLM_DENSE_WIDTH
     t0 = time.time()
@@ -300,8 +355,8 @@ def mx_records(glm, torch, wl, args):
         res[key] = {"workload": w.name, "tokens": w.T, "value": round(w.T * steps / e, 1),
                     "unit": "tokens/s", "steps": steps, "ms_per_step": round(ms, 4),
                     "roofline": roof, "layer_roofline": layer, "routing_load": load,
-                    "stages_ms": {s: round(v, 4) for s, v in pc.items()}}
-        log(f"{key}: {res[key]['value']:,.0f} tokens/s, stages {pc}")
+                    "stages_ms": stages(pc), "call_ms": pc["_pct"]}
+        log(f"{key}: {res[key]['value']:,.0f} tokens/s, stages {stages(pc)}")
     del dev, ws
     torch.cuda.empty_cache()
     return res
@@ -356,7 +411,8 @@ def main():
     ms, roof, layer, load = record(wp, elapsed, args.steps, per_call, counts, "mfma",
                                    "prefill" if wp.name == "glm_prefill" else None)
     value = wp.T * args.steps / elapsed
-    log(f"prefill: {value:,.0f} tokens/s, {ms:.3f} ms/step, stages {per_call}")
+    log(f"prefill: {value:,.0f} tokens/s, {ms:.3f} ms/step, stages {stages(per_call)}")
+    route_ms = time_route(glm, torch, dev, wp, args.steps, args.warmup, ws)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -368,7 +424,7 @@ def main():
                    "routed_scale": wp.scale, "corr_bias_std": wp.bias_std,
                    "parallelism": "single GPU"},
         "roofline": roof, "layer_roofline": layer, "routing_load": load,
-        "stages_ms": {s: round(v, 4) for s, v in per_call.items()},
+        "stages_ms": stages(per_call), "call_ms": per_call["_pct"], "route_ms": route_ms,
     }
 
     if wd:
@@ -379,12 +435,14 @@ def main():
         ms2, roof2, layer2, load2 = record(wd, e2, args.decode_steps, pc2, c2, "hbm",
                                            "decode" if wd.name == "glm_decode" else None)
         v2 = wd.T * args.decode_steps / e2
-        log(f"decode: {v2:,.0f} tokens/s, {ms2:.3f} ms/step, stages {pc2}")
+        log(f"decode: {v2:,.0f} tokens/s, {ms2:.3f} ms/step, stages {stages(pc2)}")
+        route2 = time_route(glm, torch, dd, wd, args.decode_steps, args.warmup, ws)
         line["decode"] = {"workload": wd.name, "tokens": wd.T, "value": round(v2, 1),
                           "unit": "tokens/s", "steps": args.decode_steps,
                           "ms_per_step": round(ms2, 4), "roofline": roof2,
                           "layer_roofline": layer2, "routing_load": load2,
-                          "stages_ms": {s: round(v, 4) for s, v in pc2.items()}}
+                          "stages_ms": stages(pc2), "call_ms": pc2["_pct"],
+                          "route_ms": route2}
 
     if args.variants:
         line["variants"] = variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args)

@@ -365,7 +365,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Tile configurations: <BM, BN, BK, WM, WN, stages, MFMA block>.
-using CfgDecode = Cfg<32, 256, 64, 1, 4, 4, 32>;   // few rows per expert: weight streaming
+#ifndef GLM_CFG_DECODE
+#define GLM_CFG_DECODE 32, 256, 64, 1, 4, 4, 32
+#endif
+using CfgDecode = Cfg<GLM_CFG_DECODE>;  // few rows per expert: weight streaming
 using CfgMid = Cfg<128, 256, 32, 2, 2, 4, 32>;
 #ifndef GLM_CFG_BIG
 #define GLM_CFG_BIG 256, 256, 64, 2, 4, 2, 32
