@@ -18,6 +18,10 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kTokTile = 64;   // tokens per routing tile (one bit per token in a u64 mask)
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
+#ifndef GLM_XCD_BLOCK
+#define GLM_XCD_BLOCK 64
+#endif
+constexpr int kXcdBlock = GLM_XCD_BLOCK;  // consecutive logical tiles kept on one XCD (see xcd_tile)
 
 // Work item of a grouped GEMM launch: one BM x BN output tile of one group.
 struct TileDesc {
@@ -205,6 +209,29 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Workgroup -> logical tile of a grouped GEMM launch.  Workgroups are
+// dispatched round-robin over the XCDs (workgroup b on XCD b % 8).  The n
+// tiles of the list are cut into 8R blocks of about n / 8R consecutive tiles
+// (R = ceil(n / (8 kXcdBlock)) rounds), dealt to the XCDs in turn, and each
+// XCD walks its R blocks in order.  Tiles sharing an expert's gathered rows
+// or weight slice (neighbours in the list) run on one XCD and its L2, every
+// XCD gets the same number of tiles up to one, and a run of expensive tiles
+// (a hot expert's) spreads over all XCDs.  Returns -1 past the list.
+__device__ inline int xcd_tile(int n) {
+  if (n <= 0) return -1;
+  const int x = blockIdx.x % kXcds, o = blockIdx.x / kXcds;
+  const int rounds = cdiv(n, kXcds * kXcdBlock);
+  const int blk = cdiv(n, kXcds * rounds);  // 1 .. kXcdBlock
+  const int r = o / blk;
+  if (r >= rounds) return -1;
+  const int i = (x + kXcds * r) * blk + o % blk;
+  return i < n ? i : -1;
+}
+// Launch width covering every tile of a list of at most cap tiles.
+inline int xcd_grid(int cap) {
+  return kXcds * kXcdBlock * cdiv(cdiv(cap, kXcdBlock), kXcds);
+}
 
 __device__ inline float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);

@@ -71,16 +71,6 @@ struct Cfg {
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Workgroup -> logical tile.  Logical tiles are split into 8 contiguous chunks,
-// one per XCD (workgroups are dispatched round-robin over the XCDs), so tiles
-// sharing a weight slice or an activation block run on one XCD and its L2.
-__device__ inline int xcd_tile(int n) {
-  const int c = (n + kXcds - 1) / kXcds;
-  const int x = blockIdx.x % kXcds, o = blockIdx.x / kXcds;
-  if (o >= c) return -1;
-  const int i = x * c + o;
-  return i < n ? i : -1;
-}
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, DownArgs dn) {

@@ -101,14 +101,6 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return c | (neg ? 0x80u : 0u);
 }
 
-// Workgroup -> logical tile (see the bf16 kernels: contiguous chunks per XCD).
-__device__ inline int xcd_tile(int n) {
-  const int c = (n + kXcds - 1) / kXcds;
-  const int x = blockIdx.x % kXcds, o = blockIdx.x / kXcds;
-  if (o >= c) return -1;
-  const int i = x * c + o;
-  return i < n ? i : -1;
-}
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu, MxDownArgs dn) {
