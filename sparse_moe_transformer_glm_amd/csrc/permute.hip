@@ -39,6 +39,13 @@ __device__ inline void tile_order(int local, int mt, int nt_all, bool shared, in
   *nt = cb * bn + r2 / hb;
 }
 
+// First row of row tile m of a group of `rows` rows cut into mt tiles of at
+// most BM rows: the rows are split evenly (tile sizes differ by at most one),
+// so the tiles sharing a weight slice do the same work and stay in step.
+__device__ inline int tile_row0(int m, int mt, int rows) {
+  return (int)(((long long)m * rows) / mt);
+}
+
 // Single workgroup.  masks[tile][e] has bit i set when token tile*64+i chose e.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const uint64_t* __restrict__ masks, ScanParams p, int32_t* __restrict__ counts,
@@ -163,8 +170,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     tile_order(i - s_gu[g], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
-    d.row0 = m * p.gu.BM;
-    d.rows = min(p.gu.BM, rows - d.row0);
+    d.row0 = tile_row0(m, mt, rows);
+    d.rows = tile_row0(m + 1, mt, rows) - d.row0;
     d.col0 = nt * (p.gu.BN / 2);
     gu_desc[i] = d;
   }
@@ -182,8 +189,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     tile_order(i - s_dn[g], mt, p.D / p.dn.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
-    d.row0 = m * p.dn.BM;
-    d.rows = min(p.dn.BM, grows - d.row0);
+    d.row0 = tile_row0(m, mt, grows);
+    d.rows = tile_row0(m + 1, mt, grows) - d.row0;
     d.col0 = nt * p.dn.BN;
     dn_desc[i] = d;
   }
