@@ -26,7 +26,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gate_up_glm.json")
-KERNEL_SOURCES = ("gemm_bf16.hip", "common.h")
+KERNEL_SOURCES = ("gemm_bf16.hip", "common.h", "permute.hip", "glm_moe.hip")
 
 
 def kernel_source_sha():

@@ -3,6 +3,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -201,6 +204,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt immediate: vector-memory count N, other counters left alone.
 #define GLM_VMCNT(N) (((N) & 0xF) | (((N) >> 4) << 14) | (7 << 4) | (0xF << 8))
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order.
+template <int... I, class F>
+__device__ __forceinline__ void unroll_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 // Workgroup barrier after this wave's LDS operations have completed (and
 // nothing else: outstanding global loads stay in flight).

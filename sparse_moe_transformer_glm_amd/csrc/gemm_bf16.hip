@@ -67,9 +67,11 @@ struct Cfg {
   static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles must be whole DMA instructions");
   static_assert((A_INST + B_INST) % NW == 0, "every wave issues the same number of DMAs");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
+  static_assert(ST >= 2 && ST <= 8, "ring of 2 to 8 stages");
 };
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
+
 
 
 template <class C, int MODE>
@@ -82,6 +84,10 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   __shared__ __attribute__((aligned(1024))) bf16_t lds1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16_t lds2[ST > 2 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(1024))) bf16_t lds3[ST > 3 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds4[ST > 4 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds5[ST > 5 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds6[ST > 6 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds7[ST > 7 ? C::STAGE : 8];
   __shared__ int s_asg[BM];
   __shared__ float s_wt[BM];
 
@@ -157,7 +163,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   }
 
   auto stage_ptr = [&](int s) -> bf16_t* {
-    return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3;
+    return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : s == 3 ? lds3
+         : s == 4 ? lds4 : s == 5 ? lds5 : s == 6 ? lds6 : lds7;
   };
   auto issue = [&](bf16_t* st, int kt) {
 #pragma unroll
@@ -252,10 +259,10 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       }
     };
     for (int kt = 0; kt < nk; kt += ST) {
-      step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1 % ST>{}, kt + 1);
-      if constexpr (ST > 2) if (kt + 2 < nk) step(std::integral_constant<int, 2 % ST>{}, kt + 2);
-      if constexpr (ST > 3) if (kt + 3 < nk) step(std::integral_constant<int, 3 % ST>{}, kt + 3);
+      unroll<ST>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u == 0 || kt + u < nk) step(std::integral_constant<int, u>{}, kt + u);
+      });
     }
   };
   static_assert(C::KSUB % 2 == 0, "fragment slots alternate per sub-step");
@@ -356,7 +363,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // Tile configurations: <BM, BN, BK, WM, WN, stages, MFMA block>.
 #ifndef GLM_CFG_DECODE
-#define GLM_CFG_DECODE 32, 256, 64, 1, 4, 4, 32
+#define GLM_CFG_DECODE 32, 128, 64, 1, 4, 5, 16
 #endif
 using CfgDecode = Cfg<GLM_CFG_DECODE>;  // few rows per expert: weight streaming
 using CfgMid = Cfg<128, 256, 32, 2, 2, 4, 32>;

@@ -68,6 +68,7 @@ struct Cfg {
   static_assert(BM % RPI == 0 && BN % 64 == 0, "tiles must be whole DMA instructions");
   static_assert((A_INST + B_INST) % NW == 0, "every wave issues the same number of DMAs");
   static_assert(FM <= 4, "live-block dispatch covers up to 4 row blocks");
+  static_assert(ST >= 2 && ST <= 8, "ring of 2 to 8 stages");
 };
 
 // Physical 16-byte chunk of logical chunk c of row r (8 chunks per row):
@@ -75,6 +76,7 @@ struct Cfg {
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
+
 
 // Smallest s with amax <= 448 * 2^s (0 for amax == 0): with amax = f * 2^x,
 // f in [0.5, 1), it is x - 9 when f <= 0.875, else x - 8.
@@ -112,6 +114,10 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[ST > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t lds3[ST > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds4[ST > 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds5[ST > 5 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds6[ST > 6 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds7[ST > 7 ? C::STAGE : 16];
   __shared__ int s_asg[BM];
   __shared__ float s_wt[BM];
 
@@ -236,7 +242,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   }
 
   auto stage_ptr = [&](int s) -> uint8_t* {
-    return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3;
+    return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : s == 3 ? lds3
+         : s == 4 ? lds4 : s == 5 ? lds5 : s == 6 ? lds6 : lds7;
   };
   auto issue = [&](uint8_t* st, int kt) {
 #pragma unroll
@@ -341,10 +348,10 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
       }
     };
     for (int kt = 0; kt < nk; kt += ST) {
-      step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1 % ST>{}, kt + 1);
-      if constexpr (ST > 2) if (kt + 2 < nk) step(std::integral_constant<int, 2 % ST>{}, kt + 2);
-      if constexpr (ST > 3) if (kt + 3 < nk) step(std::integral_constant<int, 3 % ST>{}, kt + 3);
+      unroll<ST>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u == 0 || kt + u < nk) step(std::integral_constant<int, u>{}, kt + u);
+      });
     }
   };
   switch (live_m) {
@@ -481,7 +488,10 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
 #ifndef GLM_MX_CFG_BIG
 #define GLM_MX_CFG_BIG 256, 128, 4, 2, 3
 #endif
-using MxDecode = Cfg<32, 256, 1, 4, 4>;
+#ifndef GLM_MX_CFG_DECODE
+#define GLM_MX_CFG_DECODE 32, 256, 1, 4, 4
+#endif
+using MxDecode = Cfg<GLM_MX_CFG_DECODE>;
 using MxMid = Cfg<128, 256, 2, 2, 3>;
 using MxBig = Cfg<GLM_MX_CFG_BIG>;
 using MxNarrow = Cfg<32, 64, 1, 1, 4>;
