@@ -366,7 +366,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #define GLM_CFG_DECODE 32, 128, 64, 1, 4, 5, 16
 #endif
 using CfgDecode = Cfg<GLM_CFG_DECODE>;  // few rows per expert: weight streaming
-using CfgMid = Cfg<128, 256, 32, 2, 2, 4, 32>;
+#ifndef GLM_CFG_MID
+#define GLM_CFG_MID 128, 256, 64, 2, 4, 3, 32
+#endif
+using CfgMid = Cfg<GLM_CFG_MID>;
 #ifndef GLM_CFG_BIG
 #define GLM_CFG_BIG 256, 256, 64, 2, 4, 2, 32
 #endif
@@ -399,7 +402,10 @@ using namespace gemm;
 GemmShape gemm_shape(double rows_per_group, bool wide) {
   if (!wide) return {CfgNarrow::BM, CfgNarrow::BN};
   if (rows_per_group <= 24.0) return {CfgDecode::BM, CfgDecode::BN};
-  if (rows_per_group <= 96.0) return {CfgMid::BM, CfgMid::BN};
+#ifndef GLM_MID_MAX_ROWS
+#define GLM_MID_MAX_ROWS 160.0
+#endif
+  if (rows_per_group <= GLM_MID_MAX_ROWS) return {CfgMid::BM, CfgMid::BN};
   return {CfgBig::BM, CfgBig::BN};
 }
 
