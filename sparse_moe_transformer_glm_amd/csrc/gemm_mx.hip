@@ -492,7 +492,10 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
 #define GLM_MX_CFG_DECODE 32, 256, 1, 4, 4
 #endif
 using MxDecode = Cfg<GLM_MX_CFG_DECODE>;
-using MxMid = Cfg<128, 256, 2, 2, 3>;
+#ifndef GLM_MX_CFG_MID
+#define GLM_MX_CFG_MID 128, 256, 2, 4, 3
+#endif
+using MxMid = Cfg<GLM_MX_CFG_MID>;
 using MxBig = Cfg<GLM_MX_CFG_BIG>;
 using MxNarrow = Cfg<32, 64, 1, 1, 4>;
 
@@ -522,7 +525,10 @@ GemmShape gemm_shape_mx(double rows_per_group, bool wide) {
   using namespace gemm_mx;
   if (!wide) return {MxNarrow::BM, MxNarrow::BN};
   if (rows_per_group <= 24.0) return {MxDecode::BM, MxDecode::BN};
-  if (rows_per_group <= 96.0) return {MxMid::BM, MxMid::BN};
+#ifndef GLM_MX_MID_MAX_ROWS
+#define GLM_MX_MID_MAX_ROWS 160.0
+#endif
+  if (rows_per_group <= GLM_MX_MID_MAX_ROWS) return {MxMid::BM, MxMid::BN};
   return {MxBig::BM, MxBig::BN};
 }
 
