@@ -315,6 +315,22 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
         log(f"{key}: {res[key]['value']:,.0f} tokens/s, hot share {res[key]['hot_share']}, "
             f"stages {stages(pc)}")
         del d
+    # the layer between the decode and prefill sizes (same weights, near-uniform
+    # routing); the roofline is whichever of MFMA and HBM binds at that size
+    sweep = {}
+    for T in (256, 1024, 2048, 4096):
+        w = wp.with_(name=f"glm_T{T}", T=T)
+        d = dev.with_x(to_device(wl.make_x(w)), to_device(wl.make_corr_bias(w)), w)
+        e, pc, c = time_layer(glm, torch, d, w, args.steps, args.warmup, ws)
+        _, _, lf, lb, _ = algorithmic(w, c)
+        bound = "mfma" if lf / (PEAK_BF16_TFLOPS * 1e12) > lb / (PEAK_HBM_GBS * 1e9) else "hbm"
+        ms, roof, layer, load = record(w, e, args.steps, pc, c, bound)
+        sweep[str(T)] = {"value": round(T * args.steps / e, 1), "unit": "tokens/s",
+                         "ms_per_step": round(ms, 4), "roofline": roof, "layer_roofline": layer,
+                         "routing_load": load, "call_ms": pc["_pct"]}
+        log(f"T={T}: {sweep[str(T)]['value']:,.0f} tokens/s, {roof['bound']} frac {roof['frac']}")
+        del d
+    res["token_sweep"] = sweep
     # dense FFN of the leading dense layers (width: see workloads.GLM_DENSE_WIDTH)
     F = wl.GLM_DENSE_WIDTH
     t0 = time.time()
