@@ -403,7 +403,7 @@ GemmShape gemm_shape(double rows_per_group, bool wide) {
   if (!wide) return {CfgNarrow::BM, CfgNarrow::BN};
   if (rows_per_group <= 24.0) return {CfgDecode::BM, CfgDecode::BN};
 #ifndef GLM_MID_MAX_ROWS
-#define GLM_MID_MAX_ROWS 160.0
+#define GLM_MID_MAX_ROWS 96.0
 #endif
   if (rows_per_group <= GLM_MID_MAX_ROWS) return {CfgMid::BM, CfgMid::BN};
   return {CfgBig::BM, CfgBig::BN};

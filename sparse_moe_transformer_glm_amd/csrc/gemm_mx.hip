@@ -526,7 +526,7 @@ GemmShape gemm_shape_mx(double rows_per_group, bool wide) {
   if (!wide) return {MxNarrow::BM, MxNarrow::BN};
   if (rows_per_group <= 24.0) return {MxDecode::BM, MxDecode::BN};
 #ifndef GLM_MX_MID_MAX_ROWS
-#define GLM_MX_MID_MAX_ROWS 160.0
+#define GLM_MX_MID_MAX_ROWS 96.0
 #endif
   if (rows_per_group <= GLM_MX_MID_MAX_ROWS) return {MxMid::BM, MxMid::BN};
   return {MxBig::BM, MxBig::BN};

@@ -40,10 +40,13 @@ __device__ inline void tile_order(int local, int mt, int nt_all, bool shared, in
 }
 
 // First row of row tile m of a group of `rows` rows cut into mt tiles of at
-// most BM rows: the rows are split evenly (tile sizes differ by at most one),
-// so the tiles sharing a weight slice do the same work and stay in step.
-__device__ inline int tile_row0(int m, int mt, int rows) {
-  return (int)(((long long)m * rows) / mt);
+// most BM rows.  The rows are dealt out evenly in units of `gran` rows (the
+// MFMA row blocks of both wave rows): the tiles sharing a weight slice do
+// nearly the same work and stay in step, and no tile computes more MFMA row
+// blocks than the group needs.
+__device__ inline int tile_row0(int m, int mt, int rows, int gran) {
+  const int units = cdiv(rows, gran);
+  return min(rows, (int)(((long long)m * units) / mt) * gran);
 }
 
 // Single workgroup.  masks[tile][e] has bit i set when token tile*64+i chose e.
@@ -170,8 +173,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     tile_order(i - s_gu[g], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
-    d.row0 = tile_row0(m, mt, rows);
-    d.rows = tile_row0(m + 1, mt, rows) - d.row0;
+    const int gran = min(64, p.gu.BM);
+    d.row0 = tile_row0(m, mt, rows, gran);
+    d.rows = tile_row0(m + 1, mt, rows, gran) - d.row0;
     d.col0 = nt * (p.gu.BN / 2);
     gu_desc[i] = d;
   }
@@ -189,8 +193,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     tile_order(i - s_dn[g], mt, p.D / p.dn.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
-    d.row0 = tile_row0(m, mt, grows);
-    d.rows = tile_row0(m + 1, mt, grows) - d.row0;
+    const int gran = min(64, p.dn.BM);
+    d.row0 = tile_row0(m, mt, grows, gran);
+    d.rows = tile_row0(m + 1, mt, grows, gran) - d.row0;
     d.col0 = nt * p.dn.BN;
     dn_desc[i] = d;
   }
