@@ -298,6 +298,36 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     const bool shared = (g == gu.E);
     const int F = shared ? gu.Fs : gu.F;
     bf16_t* Hb = shared ? gu.Hs + (size_t)row0 * F : gu.H + (size_t)(gu.offsets[g] + row0) * F;
+    constexpr int HC = TN / 2;  // hidden columns of this wave
+    if constexpr (NW * MB * HC * 2 <= C::STAGE * 2 && HC % 8 == 0 &&
+                  MB % (kWave / (HC / 8 > 0 ? HC / 8 : 1)) == 0) {
+      // Through LDS, one MB-row block at a time (as the down epilogue):
+      // 16-byte stores of 8 consecutive hidden values.
+      bf16_t* blk = lds0 + wave * (MB * HC);
+      constexpr int CG = HC / 8, RPP = kWave / CG;
+      static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
+      const int hcol0 = col0 + wn * HC;
+      __syncthreads();  // every wave is done reading the stages
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const int rb = row_of(m, r) - (wrow0 + m * MB);
+            const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
+            blk[rb * HC + q * MB + lr] = f32_to_bf16(h);
+          }
+#pragma unroll
+        for (int pass = 0; pass < MB / RPP; ++pass) {
+          const int rb = pass * RPP + lane / CG, cg = lane % CG;
+          const int row = wrow0 + m * MB + rb;
+          const uint4 v = *reinterpret_cast<const uint4*>(blk + rb * HC + 8 * cg);
+          if (row < rows) *reinterpret_cast<uint4*>(Hb + (size_t)row * F + hcol0 + 8 * cg) = v;
+        }
+      }
+    } else {
 #pragma unroll
     for (int m = 0; m < FM; ++m) {
       if (m >= live_m) continue;
@@ -311,6 +341,37 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
             const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
             Hb[(size_t)row * F + hcol] = f32_to_bf16(h);
           }
+        }
+      }
+    }
+    }
+  } else if constexpr (NW * MB * TN * 4 <= C::STAGE * 2) {
+    // Through LDS, one MB-row block at a time: each wave writes its block
+    // (MB x TN fp32) to its own slice of stage 0, then stores whole 16-byte
+    // column groups, so a store instruction covers a few full row pieces.
+    float* blk = reinterpret_cast<float*>(lds0) + wave * (MB * TN);
+    constexpr int CG = TN / 4;            // 16-byte column groups per row
+    constexpr int RPP = kWave / CG;       // rows per pass
+    static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
+    __syncthreads();  // every wave is done reading the stages
+#pragma unroll
+    for (int m = 0; m < FM; ++m) {
+      if (m >= live_m) continue;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int rb = row_of(m, r) - (wrow0 + m * MB);
+#pragma unroll
+        for (int n = 0; n < FN; ++n) blk[rb * TN + n * MB + lr] = acc[m][n][r];
+      }
+#pragma unroll
+      for (int pass = 0; pass < MB / RPP; ++pass) {
+        const int rb = pass * RPP + lane / CG, cg = lane % CG;
+        const int row = wrow0 + m * MB + rb;
+        const float4 v = *reinterpret_cast<const float4*>(blk + rb * TN + 4 * cg);
+        if (row < rows) {
+          const float w = s_wt[row];
+          float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
+          *reinterpret_cast<float4*>(y) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
         }
       }
     }
