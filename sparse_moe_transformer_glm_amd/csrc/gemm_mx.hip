@@ -399,17 +399,35 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
       }
     }
   } else {
+    // One 16-row half of a 32-row block at a time through this wave's slice
+    // of stage 0, leaving as 16-byte pieces of four consecutive columns.
+    constexpr int CG = TN / 4, RPP = kWave / CG;
+    static_assert(kWave % CG == 0 && 16 % RPP == 0 && NW * 16 * TN * 4 <= C::STAGE,
+                  "epilogue shape");
+    float* blk = reinterpret_cast<float*>(lds0) + wave * (16 * TN);
+    __syncthreads();  // every wave is done reading the stages
 #pragma unroll
     for (int m = 0; m < FM; ++m) {
       if (m >= live_m) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_of(m, r);
-        if (row < rows) {
-          const float w = s_wt[row];
-          float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
+      for (int half = 0; half < 2; ++half) {
+        // r in [8 half, 8 half + 8) covers rows [16 half, 16 half + 16) of the block
 #pragma unroll
-          for (int n = 0; n < FN; ++n) y[n * 32] = w * acc[m][n][r];
+        for (int r = 8 * half; r < 8 * half + 8; ++r) {
+          const int rb = row_of(m, r) - (wrow0 + m * 32 + 16 * half);
+#pragma unroll
+          for (int n = 0; n < FN; ++n) blk[rb * TN + n * 32 + lr] = acc[m][n][r];
+        }
+#pragma unroll
+        for (int pass = 0; pass < 16 / RPP; ++pass) {
+          const int rb = pass * RPP + lane / CG, cg = lane % CG;
+          const int row = wrow0 + m * 32 + 16 * half + rb;
+          const float4 v = *reinterpret_cast<const float4*>(blk + rb * TN + 4 * cg);
+          if (row < rows) {
+            const float w = s_wt[row];
+            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
+            *reinterpret_cast<float4*>(y) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+          }
         }
       }
     }
