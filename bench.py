@@ -386,7 +386,7 @@ def main():
     ap.add_argument("--workload", default="glm_prefill")
     ap.add_argument("--decode-workload", default="glm_decode", help="'' to skip")
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--cpu-tokens", type=int, default=100, help="0 to skip the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=120, help="0 to skip the oracle baseline")
     ap.add_argument("--no-variants", dest="variants", action="store_false",
                     help="skip the block / group-routing / dense-FFN measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
