@@ -279,7 +279,8 @@ def _sample(T, n, extra=()):
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,n_sample", [("glm_decode", None), ("glm_prefill", 24),
-                                           ("glm_skew", 16), ("glm_skew_mild", 16)])
+                                           ("glm_chunk_2k", 16), ("glm_skew", 16),
+                                           ("glm_skew_mild", 16)])
 def test_glm_shape(glm_layer, name, n_sample):
     L, dev = _glm_case(glm_layer, name)
     t0 = time.time()

@@ -89,6 +89,10 @@ WORKLOADS = {
     "glm_prefill": Workload("glm_prefill", T=8192, D=6144, E=256, k=8, F=2048, Fs=2048,
                             dtype="bf16", scale=2.5, bias_std=0.01, seed=4,
                             weight_seed=GLM_WEIGHT_SEED),
+    # GLM-5.2 shape, 2048-token chunk (about 64 rows per expert: middle tiles)
+    "glm_chunk_2k": Workload("glm_chunk_2k", T=2048, D=6144, E=256, k=8, F=2048, Fs=2048,
+                             dtype="bf16", scale=2.5, bias_std=0.01, seed=6,
+                             weight_seed=GLM_WEIGHT_SEED),
     # GLM-5.2 shape, 4096 tokens, +1.5 bias on experts 0..15 (literal skew)
     "glm_skew": Workload("glm_skew", T=4096, D=6144, E=256, k=8, F=2048, Fs=2048, dtype="bf16",
                          scale=2.5, bias_std=0.05, seed=5, weight_seed=GLM_WEIGHT_SEED,
