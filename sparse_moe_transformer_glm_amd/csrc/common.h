@@ -29,7 +29,8 @@ constexpr int kXcdBlock = GLM_XCD_BLOCK;  // consecutive logical tiles kept on o
 // Work item of a grouped GEMM launch: one BM x BN output tile of one group.
 struct TileDesc {
   int32_t group;   // expert id; E means the shared expert
-  int32_t row0;    // first row of the tile inside the group's rows
+  int32_t row0;    // first row of the tile: routed groups count in the expert-sorted
+                   // rows (the group's offset included), the shared expert in tokens
   int32_t rows;    // valid rows in the tile (1..BM)
   int32_t col0;    // first output column (gate/up: first hidden column)
 };
@@ -76,16 +77,16 @@ hipError_t launch_scan(const uint64_t* masks, const ScanParams& p,
                        TileDesc* gu_desc, int32_t* gu_count,
                        TileDesc* dn_desc, int32_t* dn_count, hipStream_t s);
 
-// Stable expert-major permutation: row_assign[row] = t * k + j.
+// Stable expert-major permutation: row_assign[row] = t * k + j, and the
+// routing weight of that row, row_w[row] = topk_w[t * k + j].
 hipError_t launch_scatter(const int32_t* topk_idx, const uint64_t* masks,
-                          const int32_t* tile_base, int T, int E, int k,
-                          int32_t* row_assign, hipStream_t s);
+                          const int32_t* tile_base, const float* topk_w, int T, int E, int k,
+                          int32_t* row_assign, float* row_w, hipStream_t s);
 
 // bf16 grouped GEMMs.
 struct GateUpArgs {
   const bf16_t* x;             // [T][D]
   const int32_t* row_assign;   // [T*k]
-  const int32_t* offsets;      // [E+1]
   const bf16_t* w1;            // [E][F][D]
   const bf16_t* w3;
   const bf16_t* sw1;           // [Fs][D]
@@ -108,10 +109,9 @@ struct DownArgs {
   const bf16_t* H;             // [T*k][F]
   const bf16_t* Hs;            // [T][Fs]
   const int32_t* row_assign;
-  const int32_t* offsets;
   const bf16_t* w2;            // [E][D][F]
   const bf16_t* sw2;           // [D][Fs]
-  const float* topk_w;         // [T*k]
+  const float* row_w;          // [T*k] routing weight of each expert-sorted row
   const TileDesc* desc;        // routed groups, then the shared expert (group E)
   const int32_t* desc_count;
   float* Y;                    // [T][k+1][D]: slot j < k routed (weighted), slot k shared
@@ -133,7 +133,6 @@ struct MxGateUpArgs {
   const uint8_t* xs;           // [D/128][T][4] (scales K-step-major)
   const uint8_t* xsp;          // [D/128][T*k][4]: the same scales in expert-row order
   const int32_t* row_assign;
-  const int32_t* offsets;
   const uint8_t* w1; const uint8_t* w1s;   // [E][F][D], [E][D/128][F][4]
   const uint8_t* w3; const uint8_t* w3s;
   const uint8_t* sw1; const uint8_t* sw1s; // [Fs][D], [D/128][Fs][4]
@@ -149,10 +148,9 @@ struct MxDownArgs {
   const uint8_t* H; const uint8_t* Hsc;
   const uint8_t* Hs; const uint8_t* Hssc;
   const int32_t* row_assign;
-  const int32_t* offsets;
   const uint8_t* w2; const uint8_t* w2s;   // [E][D][F], [E][F/128][D][4]
   const uint8_t* sw2; const uint8_t* sw2s; // [D][Fs], [Fs/128][D][4]
-  const float* topk_w;
+  const float* row_w;
   const TileDesc* desc;
   const int32_t* desc_count;
   float* Y;                    // as DownArgs

@@ -124,11 +124,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       const int rr = min(r, rows - 1);  // rows past the tile repeat its last row
       if constexpr (MODE == GATE_UP) {
         const int tok = (g == gu.E) ? row0 + rr
-                                    : gu.row_assign[gu.offsets[g] + row0 + rr] / gu.k;
+                                    : gu.row_assign[row0 + rr] / gu.k;
         base = gu.x + (size_t)tok * gu.D;
       } else {
         base = (g == dn.E) ? dn.Hs + (size_t)(row0 + rr) * dn.Fs
-                           : dn.H + (size_t)(dn.offsets[g] + row0 + rr) * dn.F;
+                           : dn.H + (size_t)(row0 + rr) * dn.F;
       }
     } else {
       const int n = r - BM;
@@ -145,20 +145,17 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     src[i] = base + ch * 8;
   }
 
-  // per-row data of the epilogue, staged once per tile
-  // (row of Y and routing weight of every row of the tile)
+  // Per-row data of the down epilogue (assignment and routing weight of row
+  // `tid` of the tile): loaded into registers before the first copies are
+  // issued and written to LDS only at the epilogue, so the loads' latency
+  // stays off the path to the first K step.
+  static_assert(BM <= C::NT, "one epilogue row per thread");
+  int row_a = 0;
+  float row_wt = 1.0f;
   if constexpr (MODE == DOWN) {
-    for (int r = tid; r < BM; r += C::NT) {
-      if (r < rows) {
-        if (g == dn.E) {
-          s_asg[r] = (row0 + r) * (dn.k + 1) + dn.k;
-          s_wt[r] = 1.0f;
-        } else {
-          const int a = dn.row_assign[dn.offsets[g] + row0 + r];
-          s_asg[r] = y_row(a, dn.k);
-          s_wt[r] = dn.topk_w[a];
-        }
-      }
+    if (tid < rows && g != dn.E) {
+      row_a = dn.row_assign[row0 + tid];
+      row_wt = dn.row_w[row0 + tid];
     }
   }
 
@@ -297,7 +294,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   if constexpr (MODE == GATE_UP) {
     const bool shared = (g == gu.E);
     const int F = shared ? gu.Fs : gu.F;
-    bf16_t* Hb = shared ? gu.Hs + (size_t)row0 * F : gu.H + (size_t)(gu.offsets[g] + row0) * F;
+    bf16_t* Hb = (shared ? gu.Hs : gu.H) + (size_t)row0 * F;
     constexpr int HC = TN / 2;  // hidden columns of this wave
     if constexpr (NW * MB * HC * 2 <= C::STAGE * 2 && HC % 8 == 0 &&
                   MB % (kWave / (HC / 8 > 0 ? HC / 8 : 1)) == 0) {
@@ -345,48 +342,55 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       }
     }
     }
-  } else if constexpr (NW * MB * TN * 4 <= C::STAGE * 2) {
-    // Through LDS, one MB-row block at a time: each wave writes its block
-    // (MB x TN fp32) to its own slice of stage 0, then stores whole 16-byte
-    // column groups, so a store instruction covers a few full row pieces.
-    float* blk = reinterpret_cast<float*>(lds0) + wave * (MB * TN);
-    constexpr int CG = TN / 4;            // 16-byte column groups per row
-    constexpr int RPP = kWave / CG;       // rows per pass
-    static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
-    __syncthreads();  // every wave is done reading the stages
+  } else {
+    // row of Y and routing weight of every row of the tile
+    if (tid < rows) {
+      s_asg[tid] = g == dn.E ? (row0 + tid) * (dn.k + 1) + dn.k : y_row(row_a, dn.k);
+      s_wt[tid] = row_wt;
+    }
+    __syncthreads();  // the row table is complete and every wave is done reading the stages
+    if constexpr (NW * MB * TN * 4 <= C::STAGE * 2) {
+      // Through LDS, one MB-row block at a time: each wave writes its block
+      // (MB x TN fp32) to its own slice of stage 0, then stores whole 16-byte
+      // column groups, so a store instruction covers a few full row pieces.
+      float* blk = reinterpret_cast<float*>(lds0) + wave * (MB * TN);
+      constexpr int CG = TN / 4;            // 16-byte column groups per row
+      constexpr int RPP = kWave / CG;       // rows per pass
+      static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
 #pragma unroll
-    for (int m = 0; m < FM; ++m) {
-      if (m >= live_m) continue;
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int rb = row_of(m, r) - (wrow0 + m * MB);
+        for (int r = 0; r < NR; ++r) {
+          const int rb = row_of(m, r) - (wrow0 + m * MB);
 #pragma unroll
-        for (int n = 0; n < FN; ++n) blk[rb * TN + n * MB + lr] = acc[m][n][r];
-      }
+          for (int n = 0; n < FN; ++n) blk[rb * TN + n * MB + lr] = acc[m][n][r];
+        }
 #pragma unroll
-      for (int pass = 0; pass < MB / RPP; ++pass) {
-        const int rb = pass * RPP + lane / CG, cg = lane % CG;
-        const int row = wrow0 + m * MB + rb;
-        const float4 v = *reinterpret_cast<const float4*>(blk + rb * TN + 4 * cg);
-        if (row < rows) {
-          const float w = s_wt[row];
-          float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
-          *reinterpret_cast<float4*>(y) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+        for (int pass = 0; pass < MB / RPP; ++pass) {
+          const int rb = pass * RPP + lane / CG, cg = lane % CG;
+          const int row = wrow0 + m * MB + rb;
+          const float4 v = *reinterpret_cast<const float4*>(blk + rb * TN + 4 * cg);
+          if (row < rows) {
+            const float w = s_wt[row];
+            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
+            *reinterpret_cast<float4*>(y) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+          }
         }
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int m = 0; m < FM; ++m) {
-      if (m >= live_m) continue;
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int row = row_of(m, r);
-        if (row < rows) {
-          const float w = s_wt[row];
-          float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
+        for (int r = 0; r < NR; ++r) {
+          const int row = row_of(m, r);
+          if (row < rows) {
+            const float w = s_wt[row];
+            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
 #pragma unroll
-          for (int n = 0; n < FN; ++n) y[n * MB] = w * acc[m][n][r];
+            for (int n = 0; n < FN; ++n) y[n * MB] = w * acc[m][n][r];
+          }
         }
       }
     }

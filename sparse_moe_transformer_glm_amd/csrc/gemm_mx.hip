@@ -151,7 +151,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
         *sc = gu.xs + (size_t)(row0 + rr) * 4;
         *sstep = (size_t)gu.T * 4;
       } else {
-        const int r = gu.offsets[g] + row0 + rr;
+        const int r = row0 + rr;
         *data = gu.xq + (size_t)(gu.row_assign[r] / gu.k) * K;
         *sc = gu.xsp + (size_t)r * 4;
         *sstep = (size_t)gu.T * gu.k * 4;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
       *sc = dn.Hssc + (size_t)(row0 + rr) * 4;
       *sstep = (size_t)dn.T * 4;
     } else {
-      const size_t r = (size_t)(dn.offsets[g] + row0 + rr);
+      const size_t r = (size_t)(row0 + rr);
       *data = dn.H + r * K;
       *sc = dn.Hsc + r * 4;
       *sstep = (size_t)dn.T * dn.k * 4;
@@ -226,18 +226,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     }
   }
 
+  // Per-row data of the down epilogue, loaded into registers here and written
+  // to LDS at the epilogue (the loads stay off the path to the first K step).
+  static_assert(BM <= C::NT, "one epilogue row per thread");
+  int row_a = 0;
+  float row_wt = 1.0f;
   if constexpr (MODE == DOWN) {
-    for (int r = tid; r < BM; r += C::NT) {
-      if (r < rows) {
-        if (g == dn.E) {
-          s_asg[r] = (row0 + r) * (dn.k + 1) + dn.k;
-          s_wt[r] = 1.0f;
-        } else {
-          const int a = dn.row_assign[dn.offsets[g] + row0 + r];
-          s_asg[r] = y_row(a, dn.k);
-          s_wt[r] = dn.topk_w[a];
-        }
-      }
+    if (tid < rows && g != dn.E) {
+      row_a = dn.row_assign[row0 + tid];
+      row_wt = dn.row_w[row0 + tid];
     }
   }
 
@@ -369,7 +366,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   if constexpr (MODE == GATE_UP) {
     const bool shared = (g == gu.E);
     const int F = shared ? gu.Fs : gu.F;
-    const size_t hrow0 = shared ? (size_t)row0 : (size_t)(gu.offsets[g] + row0);
+    const size_t hrow0 = (size_t)row0;
     uint8_t* Hq = (shared ? gu.Hs : gu.H) + hrow0 * F;
     // K-step-major scales over all rows of H (T * k) or Hs (T)
     const size_t hrows = shared ? (size_t)gu.T : (size_t)gu.T * gu.k;
@@ -405,7 +402,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     static_assert(kWave % CG == 0 && 16 % RPP == 0 && NW * 16 * TN * 4 <= C::STAGE,
                   "epilogue shape");
     float* blk = reinterpret_cast<float*>(lds0) + wave * (16 * TN);
-    __syncthreads();  // every wave is done reading the stages
+    // row of Y and routing weight of every row of the tile
+    if (tid < rows) {
+      s_asg[tid] = g == dn.E ? (row0 + tid) * (dn.k + 1) + dn.k : y_row(row_a, dn.k);
+      s_wt[tid] = row_wt;
+    }
+    __syncthreads();  // the row table is complete and every wave is done reading the stages
 #pragma unroll
     for (int m = 0; m < FM; ++m) {
       if (m >= live_m) continue;

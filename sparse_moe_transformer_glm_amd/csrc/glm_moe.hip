@@ -43,7 +43,7 @@ struct Plan {
   float norm_eps;
   bool add_residual;
   size_t xnorm, partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
-      dn_desc, row_assign, H, Hs, Y, xq, xs, xsp, Hsc, Hssc;
+      dn_desc, row_assign, row_w, H, Hs, Y, xq, xs, xsp, Hsc, Hssc;
   size_t total;
 };
 
@@ -180,6 +180,7 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   P.gu_desc = take((size_t)P.gu_cap * sizeof(TileDesc));
   P.dn_desc = take((size_t)P.dn_cap * sizeof(TileDesc));
   P.row_assign = take((size_t)A * 4);
+  P.row_w = take((size_t)A * 4);
   P.H = take((size_t)A * P.F * hid);
   P.Hs = take((size_t)T * P.Fs * hid);
   P.Y = take((size_t)T * (P.k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
@@ -295,6 +296,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   TileDesc* gu_desc = at<TileDesc>(ws, P.gu_desc);
   TileDesc* dn_desc = at<TileDesc>(ws, P.dn_desc);
   int32_t* row_assign = at<int32_t>(ws, P.row_assign);
+  float* row_w = at<float>(ws, P.row_w);
   float* Y = at<float>(ws, P.Y);
   const void* residual = P.add_residual ? x : nullptr;
 
@@ -308,7 +310,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCAN));
   GLM_HIP(launch_scan(masks, sp, counts, offsets, tile_base, gu_desc, gu_count, dn_desc, dn_count, s));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));
-  if (!P.dense) GLM_HIP(launch_scatter(idx, masks, tile_base, P.T, P.E, P.k, row_assign, s));
+  if (!P.dense) GLM_HIP(launch_scatter(idx, masks, tile_base, wts, P.T, P.E, P.k, row_assign, row_w, s));
 
   if (P.mx) {
     uint8_t* xq = at<uint8_t>(ws, P.xq);
@@ -319,7 +321,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     GLM_HIP(launch_permute_mx_scales(xs, row_assign, P.T, P.k, P.D, xsp, s));
     MxGateUpArgs ga{};
     ga.xq = xq; ga.xs = xs; ga.xsp = xsp;
-    ga.row_assign = row_assign; ga.offsets = offsets;
+    ga.row_assign = row_assign;
     ga.w1 = static_cast<const uint8_t*>(w1); ga.w1s = W.w1s;
     ga.w3 = static_cast<const uint8_t*>(w3); ga.w3s = W.w3s;
     ga.sw1 = static_cast<const uint8_t*>(shared_w1); ga.sw1s = W.sw1s;
@@ -333,10 +335,10 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
 
     MxDownArgs da{};
     da.H = ga.H; da.Hsc = ga.Hsc; da.Hs = ga.Hs; da.Hssc = ga.Hssc;
-    da.row_assign = row_assign; da.offsets = offsets;
+    da.row_assign = row_assign;
     da.w2 = static_cast<const uint8_t*>(w2); da.w2s = W.w2s;
     da.sw2 = static_cast<const uint8_t*>(shared_w2); da.sw2s = W.sw2s;
-    da.topk_w = wts; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
+    da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
     da.grid = xcd_grid(P.dn_cap);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
@@ -347,7 +349,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   } else if (P.bf16) {
     GateUpArgs ga{};
     ga.x = static_cast<const bf16_t*>(xin);
-    ga.row_assign = row_assign; ga.offsets = offsets;
+    ga.row_assign = row_assign;
     ga.w1 = static_cast<const bf16_t*>(w1); ga.w3 = static_cast<const bf16_t*>(w3);
     ga.sw1 = static_cast<const bf16_t*>(shared_w1); ga.sw3 = static_cast<const bf16_t*>(shared_w3);
     ga.desc = gu_desc; ga.desc_count = gu_count;
@@ -358,9 +360,9 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     GLM_HIP(launch_gateup_bf16(ga, P.gu, s));
 
     DownArgs da{};
-    da.H = ga.H; da.Hs = ga.Hs; da.row_assign = row_assign; da.offsets = offsets;
+    da.H = ga.H; da.Hs = ga.Hs; da.row_assign = row_assign;
     da.w2 = static_cast<const bf16_t*>(w2); da.sw2 = static_cast<const bf16_t*>(shared_w2);
-    da.topk_w = wts; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
+    da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
     da.grid = xcd_grid(P.dn_cap);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));

@@ -174,8 +174,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     TileDesc d;
     d.group = g;
     const int gran = min(64, p.gu.BM);
-    d.row0 = tile_row0(m, mt, rows, gran);
-    d.rows = tile_row0(m + 1, mt, rows, gran) - d.row0;
+    const int r0 = tile_row0(m, mt, rows, gran);
+    d.row0 = (g < E ? s_off[g] : 0) + r0;
+    d.rows = tile_row0(m + 1, mt, rows, gran) - r0;
     d.col0 = nt * (p.gu.BN / 2);
     gu_desc[i] = d;
   }
@@ -194,8 +195,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     TileDesc d;
     d.group = g;
     const int gran = min(64, p.dn.BM);
-    d.row0 = tile_row0(m, mt, grows, gran);
-    d.rows = tile_row0(m + 1, mt, grows, gran) - d.row0;
+    const int r0 = tile_row0(m, mt, grows, gran);
+    d.row0 = (g < E ? s_off[g] : 0) + r0;
+    d.rows = tile_row0(m + 1, mt, grows, gran) - r0;
     d.col0 = nt * p.dn.BN;
     dn_desc[i] = d;
   }
@@ -205,8 +207,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 // expert e is the number of lower lanes whose mask bit is set.
 __global__ __launch_bounds__(64) void scatter_kernel(
     const int32_t* __restrict__ topk_idx, const uint64_t* __restrict__ masks,
-    const int32_t* __restrict__ tile_base, int T, int E, int k,
-    int32_t* __restrict__ row_assign) {
+    const int32_t* __restrict__ tile_base, const float* __restrict__ topk_w, int T, int E,
+    int k, int32_t* __restrict__ row_assign, float* __restrict__ row_w) {
   const int tile = blockIdx.x, lane = threadIdx.x;
   const int t = tile * kTokTile + lane;
   if (t >= T) return;
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(
     const uint64_t m = masks[(size_t)tile * E + e];
     const int row = tile_base[(size_t)tile * E + e] + __popcll(m & below);
     row_assign[row] = t * k + j;
+    row_w[row] = topk_w[(size_t)t * k + j];
   }
 }
 
@@ -231,10 +234,10 @@ hipError_t launch_scan(const uint64_t* masks, const ScanParams& p, int32_t* coun
 }
 
 hipError_t launch_scatter(const int32_t* topk_idx, const uint64_t* masks,
-                          const int32_t* tile_base, int T, int E, int k, int32_t* row_assign,
-                          hipStream_t s) {
-  scatter_kernel<<<cdiv(T, kTokTile), 64, 0, s>>>(topk_idx, masks, tile_base, T, E, k,
-                                                   row_assign);
+                          const int32_t* tile_base, const float* topk_w, int T, int E, int k,
+                          int32_t* row_assign, float* row_w, hipStream_t s) {
+  scatter_kernel<<<cdiv(T, kTokTile), 64, 0, s>>>(topk_idx, masks, tile_base, topk_w, T, E, k,
+                                                   row_assign, row_w);
   return hipGetLastError();
 }
 
