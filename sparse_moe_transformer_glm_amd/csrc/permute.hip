@@ -158,19 +158,74 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     }
   }
 
-  // tile descriptors: group-major, then output-column tile, then row tile
+  // Listing order of the groups: the shared expert first, then the routed
+  // experts by rows per row tile, most first (ties: lower index).  The
+  // longest tiles start first and the shortest end the launch, which keeps
+  // the CUs' last tiles short.  s_pg / s_pd: first tile of the group listed
+  // at position p; s_og / s_od: that group.
+  __shared__ int s_pg[kMaxExperts + 1], s_og[kMaxExperts + 1];
+  __shared__ int s_pd[kMaxExperts + 1], s_od[kMaxExperts + 1];
+  // sort keys (rows per row tile, then the index, packed into one int so all
+  // keys differ) and tile counts of every routed group
+  __shared__ int s_kg[kMaxExperts], s_kd[kMaxExperts], s_tg[kMaxExperts], s_td[kMaxExperts];
+  // per group: rank and first tile in each list, summed over kParts slices
+  __shared__ int s_rank[4][kMaxExperts];
+  if (tid < kMaxExperts) {
+    const int c = tid < E ? s_cnt[tid] : 0;
+    const int mg = cdiv(c, p.gu.BM), md = cdiv(c, p.dn.BM);
+    s_kg[tid] = ((c == 0 ? 0 : c / mg) << 16) | (0xFFFF - tid);
+    s_kd[tid] = ((c == 0 ? 0 : c / md) << 16) | (0xFFFF - tid);
+    s_tg[tid] = mg * (2 * p.F / p.gu.BN);
+    s_td[tid] = md * (p.D / p.dn.BN);
+    s_rank[0][tid] = 0; s_rank[1][tid] = 0; s_rank[2][tid] = 0; s_rank[3][tid] = 0;
+  }
+  __syncthreads();
+  {
+    // thread (e, q) compares group e with the groups of slice q
+    const int per_q = cdiv(E, kParts), f0 = q * per_q, f1 = min(E, f0 + per_q);
+    if (e < E && f0 < f1) {
+      const int kg = s_kg[e], kd = s_kd[e];
+      int rg = 0, rd = 0, bg = 0, bd = 0;
+#pragma unroll 8
+      for (int f = f0; f < f1; ++f) {
+        if (s_kg[f] > kg) { ++rg; bg += s_tg[f]; }
+        if (s_kd[f] > kd) { ++rd; bd += s_td[f]; }
+      }
+      atomicAdd(&s_rank[0][e], rg);
+      atomicAdd(&s_rank[1][e], bg);
+      atomicAdd(&s_rank[2][e], rd);
+      atomicAdd(&s_rank[3][e], bd);
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int rg = s_rank[0][tid], rd = s_rank[2][tid];
+    s_og[1 + rg] = tid;  // after the shared group's tiles:
+    s_pg[1 + rg] = cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN) + s_rank[1][tid];
+    s_od[1 + rd] = tid;
+    s_pd[1 + rd] = cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) + s_rank[3][tid];
+  }
+  if (tid == 0) {
+    s_og[0] = E;
+    s_pg[0] = 0;
+    s_od[0] = E;
+    s_pd[0] = 0;
+  }
+  __syncthreads();
+
+  // tile descriptors: groups in listing order, then output-column tile, then row tile
   const int gu_total = s_gu[E + 1];
   for (int i = tid; i < gu_total; i += kScanThreads) {
-    int lo = 0, hi = E;  // largest g with s_gu[g] <= i
+    int lo = 0, hi = E;  // largest position with s_pg <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_gu[mid] <= i) lo = mid; else hi = mid - 1;
+      if (s_pg[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
+    const int g = s_og[lo];
     const int rows = g < E ? s_cnt[g] : p.T;
     const int mt = cdiv(rows, p.gu.BM);
     int nt, m;
-    tile_order(i - s_gu[g], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
+    tile_order(i - s_pg[lo], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
     const int gran = min(64, p.gu.BM);
@@ -185,13 +240,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int lo = 0, hi = E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_dn[mid] <= i) lo = mid; else hi = mid - 1;
+      if (s_pd[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
+    const int g = s_od[lo];
     const int grows = g < E ? s_cnt[g] : p.T;
     const int mt = cdiv(grows, p.dn.BM);
     int nt, m;
-    tile_order(i - s_dn[g], mt, p.D / p.dn.BN, g == E, &m, &nt);
+    tile_order(i - s_pd[lo], mt, p.D / p.dn.BN, g == E, &m, &nt);
     TileDesc d;
     d.group = g;
     const int gran = min(64, p.dn.BM);
