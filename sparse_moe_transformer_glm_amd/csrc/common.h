@@ -21,10 +21,14 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kTokTile = 64;   // tokens per routing tile (one bit per token in a u64 mask)
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
-#ifndef GLM_XCD_BLOCK
-#define GLM_XCD_BLOCK 64
+// Consecutive logical tiles kept on one XCD (see xcd_tile), per GEMM.
+#ifndef GLM_XCD_BLOCK_GU
+#define GLM_XCD_BLOCK_GU 16
 #endif
-constexpr int kXcdBlock = GLM_XCD_BLOCK;  // consecutive logical tiles kept on one XCD (see xcd_tile)
+#ifndef GLM_XCD_BLOCK_DN
+#define GLM_XCD_BLOCK_DN 64
+#endif
+constexpr int kXcdBlockGu = GLM_XCD_BLOCK_GU, kXcdBlockDn = GLM_XCD_BLOCK_DN;
 
 // Work item of a grouped GEMM launch: one BM x BN output tile of one group.
 struct TileDesc {
@@ -97,6 +101,7 @@ struct GateUpArgs {
   bf16_t* Hs;                  // [T][Fs]
   int T, D, E, F, Fs, k;
   int grid;                    // launched workgroups (>= desc_count, multiple of 8)
+  int xblk;                    // XCD block of the tile mapping (xcd_tile)
 };
 // Tile shape of a grouped GEMM launch.  `wide` says the output width allows
 // the 256-column tiles (gate/up: F and F_shared multiples of 128; down and
@@ -117,6 +122,7 @@ struct DownArgs {
   float* Y;                    // [T][k+1][D]: slot j < k routed (weighted), slot k shared
   int T, D, E, F, Fs, k;
   int grid;
+  int xblk;
 };
 hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s);
 
@@ -143,6 +149,7 @@ struct MxGateUpArgs {
   uint8_t* Hs; uint8_t* Hssc;  // [T][Fs], [Fs/128][T][4]
   int T, D, E, F, Fs, k;
   int grid;
+  int xblk;
 };
 struct MxDownArgs {
   const uint8_t* H; const uint8_t* Hsc;
@@ -156,6 +163,7 @@ struct MxDownArgs {
   float* Y;                    // as DownArgs
   int T, D, E, F, Fs, k;
   int grid;
+  int xblk;
 };
 // x (bf16 [T][D]) -> MXFP8 codes [T][D] and K-step-major scales [D/128][T][4].
 hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int T, int D,
@@ -224,24 +232,25 @@ __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 // Workgroup -> logical tile of a grouped GEMM launch.  Workgroups are
 // dispatched round-robin over the XCDs (workgroup b on XCD b % 8).  The n
 // tiles of the list are cut into 8R blocks of about n / 8R consecutive tiles
-// (R = ceil(n / (8 kXcdBlock)) rounds), dealt to the XCDs in turn, and each
+// (R = ceil(n / (8 xb)) rounds), dealt to the XCDs in turn, and each
 // XCD walks its R blocks in order.  Tiles sharing an expert's gathered rows
 // or weight slice (neighbours in the list) run on one XCD and its L2, every
 // XCD gets the same number of tiles up to one, and a run of expensive tiles
 // (a hot expert's) spreads over all XCDs.  Returns -1 past the list.
-__device__ inline int xcd_tile(int n) {
+__device__ inline int xcd_tile(int n, int xb) {
   if (n <= 0) return -1;
   const int x = blockIdx.x % kXcds, o = blockIdx.x / kXcds;
-  const int rounds = cdiv(n, kXcds * kXcdBlock);
-  const int blk = cdiv(n, kXcds * rounds);  // 1 .. kXcdBlock
+  const int rounds = cdiv(n, kXcds * xb);
+  const int blk = cdiv(n, kXcds * rounds);  // 1 .. xb
   const int r = o / blk;
   if (r >= rounds) return -1;
   const int i = (x + kXcds * r) * blk + o % blk;
   return i < n ? i : -1;
 }
-// Launch width covering every tile of a list of at most cap tiles.
-inline int xcd_grid(int cap) {
-  return kXcds * kXcdBlock * cdiv(cdiv(cap, kXcdBlock), kXcds);
+// Launch width covering every tile of a list of at most cap tiles
+// (each XCD walks at most xb * ceil(cap / 8 xb) ordinals).
+inline int xcd_grid(int cap, int xb) {
+  return kXcds * xb * cdiv(cdiv(cap, xb), kXcds);
 }
 
 __device__ inline float bf16_to_f32(bf16_t v) {

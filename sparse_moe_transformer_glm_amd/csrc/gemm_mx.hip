@@ -128,12 +128,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   // ---------------------------------------------------------- tile setup
   int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0;
   if constexpr (MODE == GATE_UP) {
-    const int i = xcd_tile(*gu.desc_count);
+    const int i = xcd_tile(*gu.desc_count, gu.xblk);
     if (i < 0) return;
     const TileDesc d = gu.desc[i];
     g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0; K = gu.D;
   } else {
-    const int i = xcd_tile(*dn.desc_count);
+    const int i = xcd_tile(*dn.desc_count, dn.xblk);
     if (i < 0) return;
     const TileDesc d = dn.desc[i];
     g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0;
