@@ -21,14 +21,16 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kTokTile = 64;   // tokens per routing tile (one bit per token in a u64 mask)
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
-// Consecutive logical tiles kept on one XCD (see xcd_tile), per GEMM.
-#ifndef GLM_XCD_BLOCK_GU
-#define GLM_XCD_BLOCK_GU 16
+// Consecutive logical tiles kept on one XCD (see xcd_tile): kXcdBlock in
+// general, kXcdBlockRoutedGu for the bf16 gate/up GEMM of routed experts on
+// 256-row tiles (measured per launch kind).
+#ifndef GLM_XCD_BLOCK
+#define GLM_XCD_BLOCK 64
 #endif
-#ifndef GLM_XCD_BLOCK_DN
-#define GLM_XCD_BLOCK_DN 64
+#ifndef GLM_XCD_BLOCK_ROUTED_GU
+#define GLM_XCD_BLOCK_ROUTED_GU 16
 #endif
-constexpr int kXcdBlockGu = GLM_XCD_BLOCK_GU, kXcdBlockDn = GLM_XCD_BLOCK_DN;
+constexpr int kXcdBlock = GLM_XCD_BLOCK, kXcdBlockRoutedGu = GLM_XCD_BLOCK_ROUTED_GU;
 
 // Work item of a grouped GEMM launch: one BM x BN output tile of one group.
 struct TileDesc {

@@ -330,7 +330,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     ga.H = at<uint8_t>(ws, P.H); ga.Hsc = at<uint8_t>(ws, P.Hsc);
     ga.Hs = at<uint8_t>(ws, P.Hs); ga.Hssc = at<uint8_t>(ws, P.Hssc);
     ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
-    ga.xblk = kXcdBlockGu;
+    ga.xblk = kXcdBlock;
     ga.grid = xcd_grid(P.gu_cap, ga.xblk);
     GLM_HIP(launch_gateup_mx(ga, P.gu, s));
 
@@ -341,7 +341,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     da.sw2 = static_cast<const uint8_t*>(shared_w2); da.sw2s = W.sw2s;
     da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
-    da.xblk = kXcdBlockDn;
+    da.xblk = kXcdBlock;
     da.grid = xcd_grid(P.dn_cap, da.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
     GLM_HIP(launch_down_mx(da, P.dn, s));
@@ -357,7 +357,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     ga.desc = gu_desc; ga.desc_count = gu_count;
     ga.H = at<bf16_t>(ws, P.H); ga.Hs = at<bf16_t>(ws, P.Hs);
     ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
-    ga.xblk = kXcdBlockGu;
+    ga.xblk = (!P.dense && P.gu.BM == 256) ? kXcdBlockRoutedGu : kXcdBlock;
     ga.grid = xcd_grid(P.gu_cap, ga.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
     GLM_HIP(launch_gateup_bf16(ga, P.gu, s));
@@ -367,7 +367,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     da.w2 = static_cast<const bf16_t*>(w2); da.sw2 = static_cast<const bf16_t*>(shared_w2);
     da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
-    da.xblk = kXcdBlockDn;
+    da.xblk = kXcdBlock;
     da.grid = xcd_grid(P.dn_cap, da.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
     GLM_HIP(launch_down_bf16(da, P.dn, s));

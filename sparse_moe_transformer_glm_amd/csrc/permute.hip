@@ -158,11 +158,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     }
   }
 
-  // Listing order of the groups: the shared expert first, then the routed
-  // experts by rows per row tile, most first (ties: lower index).  The
-  // longest tiles start first and the shortest end the launch, which keeps
-  // the CUs' last tiles short.  s_pg / s_pd: first tile of the group listed
-  // at position p; s_og / s_od: that group.
+  // Listing order of the groups.  With row tiles of more than 32 rows: the
+  // shared expert first, then the routed experts by rows per row tile, most
+  // first (ties: lower index), so the longest tiles start first and the
+  // shortest end the launch, which keeps the CUs' last tiles short.  Decode
+  // tiles (32 rows) all cost about one weight slice, so there the routed
+  // experts keep index order and the shared expert comes last.  s_pg / s_pd:
+  // first tile of the group listed at position p; s_og / s_od: that group.
   __shared__ int s_pg[kMaxExperts + 1], s_og[kMaxExperts + 1];
   __shared__ int s_pd[kMaxExperts + 1], s_od[kMaxExperts + 1];
   // sort keys (rows per row tile, then the index, packed into one int so all
@@ -170,6 +172,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __shared__ int s_kg[kMaxExperts], s_kd[kMaxExperts], s_tg[kMaxExperts], s_td[kMaxExperts];
   // per group: rank and first tile in each list, summed over kParts slices
   __shared__ int s_rank[4][kMaxExperts];
+  const bool lpt_g = p.gu.BM > 32, lpt_d = p.dn.BM > 32;
   if (tid < kMaxExperts) {
     const int c = tid < E ? s_cnt[tid] : 0;
     const int mg = cdiv(c, p.gu.BM), md = cdiv(c, p.dn.BM);
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   {
     // thread (e, q) compares group e with the groups of slice q
     const int per_q = cdiv(E, kParts), f0 = q * per_q, f1 = min(E, f0 + per_q);
-    if (e < E && f0 < f1) {
+    if ((lpt_g || lpt_d) && e < E && f0 < f1) {
       const int kg = s_kg[e], kd = s_kd[e];
       int rg = 0, rd = 0, bg = 0, bd = 0;
 #pragma unroll 8
@@ -199,17 +202,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   }
   __syncthreads();
   if (tid < E) {
-    const int rg = s_rank[0][tid], rd = s_rank[2][tid];
-    s_og[1 + rg] = tid;  // after the shared group's tiles:
-    s_pg[1 + rg] = cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN) + s_rank[1][tid];
-    s_od[1 + rd] = tid;
-    s_pd[1 + rd] = cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) + s_rank[3][tid];
+    if (lpt_g) {
+      const int rg = s_rank[0][tid];
+      s_og[1 + rg] = tid;  // after the shared group's tiles:
+      s_pg[1 + rg] = cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN) + s_rank[1][tid];
+    } else {
+      s_og[tid] = tid;
+      s_pg[tid] = s_gu[tid];
+    }
+    if (lpt_d) {
+      const int rd = s_rank[2][tid];
+      s_od[1 + rd] = tid;
+      s_pd[1 + rd] = cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) + s_rank[3][tid];
+    } else {
+      s_od[tid] = tid;
+      s_pd[tid] = s_dn[tid];
+    }
   }
   if (tid == 0) {
-    s_og[0] = E;
-    s_pg[0] = 0;
-    s_od[0] = E;
-    s_pd[0] = 0;
+    s_og[lpt_g ? 0 : E] = E;
+    s_pg[lpt_g ? 0 : E] = lpt_g ? 0 : s_gu[E];
+    s_od[lpt_d ? 0 : E] = E;
+    s_pd[lpt_d ? 0 : E] = lpt_d ? 0 : s_dn[E];
   }
   __syncthreads();
 
