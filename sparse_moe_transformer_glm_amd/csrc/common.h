@@ -14,6 +14,14 @@ namespace glm {
 // ------------------------------------------------------------ vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Store of a slot row piece that is read once, by the combine pass: a
+// non-temporal store, so the 4-byte-per-element slot rows do not displace
+// the weight and activation lines the grouped GEMMs are still reading from L2.
+__device__ __forceinline__ void store_stream(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
 
 constexpr int kWave = 64;

@@ -374,7 +374,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
           if (row < rows) {
             const float w = s_wt[row];
             float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
-            *reinterpret_cast<float4*>(y) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+            store_stream(y, f32x4{w * v.x, w * v.y, w * v.z, w * v.w});
           }
         }
       }
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
             const float w = s_wt[row];
             float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
 #pragma unroll
-            for (int n = 0; n < FN; ++n) y[n * MB] = w * acc[m][n][r];
+            for (int n = 0; n < FN; ++n) store_stream(y + n * MB, w * acc[m][n][r]);
           }
         }
       }
@@ -398,20 +398,34 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
 }
 
 // out[t][d] = Y[t][k][d] + Y[t][0][d] + ... + Y[t][k-1][d] (+ residual[t][d]),
-// four columns per thread.
-template <int RES>  // 0: none, 1: bf16 residual, 2: fp32 residual
+// four columns per thread.  KC > 0 fixes k at compile time, so every slot's
+// load is issued before the first add; KC = 0 takes k at run time.  The slot
+// rows are read once: non-temporal loads.
+template <int RES, int KC>  // RES 0: none, 1: bf16 residual, 2: fp32 residual
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       float* __restrict__ out, int T, int D,
-                                                      int k, const void* __restrict__ residual) {
+                                                      int k_rt, const void* __restrict__ residual) {
+  const int k = KC > 0 ? KC : k_rt;
   const int D4 = D / 4;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)T * D4) return;
   const int t = (int)(i / D4), c = (int)(i % D4);
-  const float4* y = reinterpret_cast<const float4*>(Y + (size_t)t * (k + 1) * D) + c;
-  float4 v = y[(size_t)k * D4];
-  for (int j = 0; j < k; ++j) {
-    const float4 u = y[(size_t)j * D4];
-    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+  const f32x4* y = reinterpret_cast<const f32x4*>(Y + (size_t)t * (k + 1) * D) + c;
+  const f32x4 vs = __builtin_nontemporal_load(y + (size_t)k * D4);
+  float4 v = make_float4(vs.x, vs.y, vs.z, vs.w);
+  if constexpr (KC > 0) {
+    f32x4 u[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) u[j] = __builtin_nontemporal_load(y + (size_t)j * D4);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      v.x += u[j].x; v.y += u[j].y; v.z += u[j].z; v.w += u[j].w;
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const f32x4 u = __builtin_nontemporal_load(y + (size_t)j * D4);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
   }
   if constexpr (RES == 1) {
     const uint2 r = reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(residual) +
@@ -487,9 +501,15 @@ hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, const
   const size_t n = (size_t)T * (D / 4);
   if (n == 0) return hipSuccess;
   const unsigned grid = (unsigned)((n + 255) / 256);
-  if (!residual) combine_kernel<0><<<grid, 256, 0, s>>>(Y, out, T, D, k, nullptr);
-  else if (res_bf16) combine_kernel<1><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
-  else combine_kernel<2><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
+  if (k == 8) {
+    if (!residual) combine_kernel<0, 8><<<grid, 256, 0, s>>>(Y, out, T, D, k, nullptr);
+    else if (res_bf16) combine_kernel<1, 8><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
+    else combine_kernel<2, 8><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
+  } else {
+    if (!residual) combine_kernel<0, 0><<<grid, 256, 0, s>>>(Y, out, T, D, k, nullptr);
+    else if (res_bf16) combine_kernel<1, 0><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
+    else combine_kernel<2, 0><<<grid, 256, 0, s>>>(Y, out, T, D, k, residual);
+  }
   return hipGetLastError();
 }
 

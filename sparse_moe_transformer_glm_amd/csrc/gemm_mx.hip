@@ -428,7 +428,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
           if (row < rows) {
             const float w = s_wt[row];
             float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
-            *reinterpret_cast<float4*>(y) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+            store_stream(y, f32x4{w * v.x, w * v.y, w * v.z, w * v.w});
           }
         }
       }
