@@ -14,14 +14,6 @@ namespace glm {
 // ------------------------------------------------------------ vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Store of a slot row piece that is read once, by the combine pass: a
-// non-temporal store, so the 4-byte-per-element slot rows do not displace
-// the weight and activation lines the grouped GEMMs are still reading from L2.
-__device__ __forceinline__ void store_stream(float* p, f32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
-}
-__device__ __forceinline__ void store_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
 typedef uint16_t bf16_t;  // bf16 bit pattern in memory
 
 constexpr int kWave = 64;
@@ -40,9 +32,33 @@ constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-ro
 #endif
 constexpr int kXcdBlock = GLM_XCD_BLOCK, kXcdBlockRoutedGu = GLM_XCD_BLOCK_ROUTED_GU;
 
+// Cache policy of the weight-row copies.  The only row tile of a group is the
+// only reader of the group's weight rows in a launch, so on decode tiles (at
+// most GLM_STREAM_B_MAX_BM rows, at least 128 columns) those rows are copied
+// with the non-temporal hint and do not displace reused lines; groups with
+// several row tiles share each weight row through L2.  The narrow 64-column
+// tiles (dense layers on decode batches) keep plain copies.
+#ifndef GLM_STREAM_B_MAX_BM
+#define GLM_STREAM_B_MAX_BM 32
+#endif
+constexpr int32_t kSoleRowTile = 1 << 16;  // TileDesc::group flag
+constexpr int32_t kGroupMask = kSoleRowTile - 1;
+constexpr int kCpolNt = 2;  // cache-policy immediate of the LDS-DMA load: NT
+template <int BM, int BN>
+constexpr bool kStreamB = BM <= GLM_STREAM_B_MAX_BM && BN >= 128;
+
+// Store of a slot row piece that is read once, by the combine pass: a
+// non-temporal store, so the 4-byte-per-element slot rows do not displace
+// the weight and activation lines the grouped GEMMs are still reading from L2.
+__device__ __forceinline__ void store_stream(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 // Work item of a grouped GEMM launch: one BM x BN output tile of one group.
 struct TileDesc {
-  int32_t group;   // expert id; E means the shared expert
+  int32_t group;   // expert id (E: the shared expert), | kSoleRowTile when the group has
+                   // one row tile, i.e. this tile is the only reader of the group's weights
   int32_t row0;    // first row of the tile: routed groups count in the expert-sorted
                    // rows (the group's offset included), the shared expert in tokens
   int32_t rows;    // valid rows in the tile (1..BM)

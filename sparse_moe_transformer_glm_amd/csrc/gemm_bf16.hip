@@ -97,16 +97,19 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
 
   // ---------------------------------------------------------- tile setup
   int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0;
+  bool sole = false;
   if constexpr (MODE == GATE_UP) {
     const int i = xcd_tile(*gu.desc_count, gu.xblk);
     if (i < 0) return;
     const TileDesc d = gu.desc[i];
-    g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0; K = gu.D;
+    g = d.group & kGroupMask; sole = d.group & kSoleRowTile; row0 = d.row0; rows = d.rows;
+    col0 = d.col0; K = gu.D;
   } else {
     const int i = xcd_tile(*dn.desc_count, dn.xblk);
     if (i < 0) return;
     const TileDesc d = dn.desc[i];
-    g = d.group; row0 = d.row0; rows = d.rows; col0 = d.col0;
+    g = d.group & kGroupMask; sole = d.group & kSoleRowTile; row0 = d.row0; rows = d.rows;
+    col0 = d.col0;
     K = (g == dn.E) ? dn.Fs : dn.F;
   }
 
@@ -169,8 +172,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       const int q = wave + i * NW;
       // (the source goes through void*: a typed pointer here silently drops
       // the kernel's host-side launch stub)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
-                                       (lds_void*)(st + q * (RPI * BK)), 16, 0, 0);
+      if (kStreamB<BM, BN> && sole && q >= C::A_INST)
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
+                                         (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
+                                         (lds_void*)(st + q * (RPI * BK)), 16, 0, 0);
     }
   };
 

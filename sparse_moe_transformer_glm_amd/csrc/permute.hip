@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int nt, m;
     tile_order(i - s_pg[lo], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
     TileDesc d;
-    d.group = g;
+    d.group = g | (mt == 1 ? kSoleRowTile : 0);
     const int gran = min(64, p.gu.BM);
     const int r0 = tile_row0(m, mt, rows, gran);
     d.row0 = (g < E ? s_off[g] : 0) + r0;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int nt, m;
     tile_order(i - s_pd[lo], mt, p.D / p.dn.BN, g == E, &m, &nt);
     TileDesc d;
-    d.group = g;
+    d.group = g | (mt == 1 ? kSoleRowTile : 0);
     const int gran = min(64, p.dn.BM);
     const int r0 = tile_row0(m, mt, grows, gran);
     d.row0 = (g < E ? s_off[g] : 0) + r0;
