@@ -39,7 +39,7 @@ constexpr int kXcdBlock = GLM_XCD_BLOCK, kXcdBlockRoutedGu = GLM_XCD_BLOCK_ROUTE
 // several row tiles share each weight row through L2.  The narrow 64-column
 // tiles (dense layers on decode batches) keep plain copies.
 #ifndef GLM_STREAM_B_MAX_BM
-#define GLM_STREAM_B_MAX_BM 32
+#define GLM_STREAM_B_MAX_BM 128
 #endif
 constexpr int32_t kSoleRowTile = 1 << 16;  // TileDesc::group flag
 constexpr int32_t kGroupMask = kSoleRowTile - 1;
