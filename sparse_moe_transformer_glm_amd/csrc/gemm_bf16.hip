@@ -66,6 +66,7 @@ struct Cfg {
   static_assert(TM % MB == 0 && TN % MB == 0, "wave tile must hold whole MFMA blocks");
   static_assert(BM % RPI == 0 && BN % RPI == 0, "tiles must be whole DMA instructions");
   static_assert((A_INST + B_INST) % NW == 0, "every wave issues the same number of DMAs");
+  static_assert(A_INST % NW == 0, "copy i of every wave is an A copy exactly when i < A_INST / NW");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
   static_assert(ST >= 2 && ST <= 8, "ring of 2 to 8 stages");
 };
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       const int q = wave + i * NW;
       // (the source goes through void*: a typed pointer here silently drops
       // the kernel's host-side launch stub)
-      if (kStreamB<BM, BN> && sole && q >= C::A_INST)
+      if (kStreamB<BM, BN> && i * NW >= C::A_INST && sole)  // a weight-row copy
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
       else

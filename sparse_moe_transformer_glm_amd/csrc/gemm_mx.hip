@@ -67,6 +67,7 @@ struct Cfg {
   static_assert(TM % 32 == 0 && TN % 64 == 0, "wave tile: whole 32-row blocks, gate/up pairs");
   static_assert(BM % RPI == 0 && BN % 64 == 0, "tiles must be whole DMA instructions");
   static_assert((A_INST + B_INST) % NW == 0, "every wave issues the same number of DMAs");
+  static_assert(A_INST % NW == 0, "copy i of every wave is an A copy exactly when i < A_INST / NW");
   static_assert(FM <= 4, "live-block dispatch covers up to 4 row blocks");
   static_assert(ST >= 2 && ST <= 8, "ring of 2 to 8 stages");
 };
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int q = wave + i * NW;
-      if (kStreamB<BM, BN> && sole && q >= C::A_INST)  // weight rows of a decode tile
+      if (kStreamB<BM, BN> && i * NW >= C::A_INST && sole)  // a weight-row copy
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
       else
