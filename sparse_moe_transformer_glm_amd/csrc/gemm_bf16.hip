@@ -167,13 +167,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : s == 3 ? lds3
          : s == 4 ? lds4 : s == 5 ? lds5 : s == 6 ? lds6 : lds7;
   };
-  auto issue = [&](bf16_t* st, int kt) {
+  // NT: weight rows go with the non-temporal hint (a sole row tile, see kStreamB)
+  auto issue = [&](bf16_t* st, int kt, auto nt_c) {
+    constexpr bool NT = decltype(nt_c)::value;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int q = wave + i * NW;
       // (the source goes through void*: a typed pointer here silently drops
       // the kernel's host-side launch stub)
-      if (kStreamB<BM, BN> && i * NW >= C::A_INST && sole)  // a weight-row copy
+      if (NT && i * NW >= C::A_INST)  // a weight-row copy
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
       else
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   // sub-step s+1 are issued before the MFMAs of sub-step s, and the stage
   // hand-over (wait, barrier, refill, next stage's first reads) sits just
   // before the last sub-step's MFMAs.
-  auto run = [&](auto live_c) {
+  auto run = [&](auto live_c, auto nt_c) {
     constexpr int LIVE = decltype(live_c)::value;
     bf16x8 fa[2][FM], fb[2][FN];
     auto load_frags = [&](const bf16_t* st, int sub, int slot) {
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     // prologue: fill every stage, wait for stage 0, read its first fragments
 #pragma unroll
     for (int s = 0; s < ST; ++s)
-      if (s < nk) issue(stage_ptr(s), s);
+      if (s < nk) issue(stage_ptr(s), s, nt_c);
     if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
           if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 2)));
           else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
           lds_barrier();
-          if (kt + ST < nk) issue(cur, kt + ST);
+          if (kt + ST < nk) issue(cur, kt + ST, nt_c);
           load_frags(stage_ptr((s + 1) % ST), 0, 0);  // slot 0 is free: sub-step KSUB-2 used it
         }
         mma(sub & 1);
@@ -272,23 +274,32 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   };
   static_assert(C::KSUB % 2 == 0, "fragment slots alternate per sub-step");
   static_assert(FM <= 4, "live-block dispatch covers up to 4 row blocks");
-  switch (live_m) {
-    case 1: run(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (FM >= 2) run(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (FM >= 3) run(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr (FM >= 4) run(std::integral_constant<int, 4>{}); break;
-    default: {
-      // this wave row holds no valid row: keep the barrier count of the others
-      for (int s = 0; s < ST; ++s)
-        if (s < nk) issue(stage_ptr(s), s);
-      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
-      lds_barrier();
-      for (int kt = 0; kt + 1 < nk; ++kt) {
+  // the main loop, specialised on the live row blocks and the copy hint
+  auto go = [&](auto nt_c) {
+    switch (live_m) {
+      case 1: run(std::integral_constant<int, 1>{}, nt_c); break;
+      case 2: if constexpr (FM >= 2) run(std::integral_constant<int, 2>{}, nt_c); break;
+      case 3: if constexpr (FM >= 3) run(std::integral_constant<int, 3>{}, nt_c); break;
+      case 4: if constexpr (FM >= 4) run(std::integral_constant<int, 4>{}, nt_c); break;
+      default: {
+        // this wave row holds no valid row: keep the barrier count of the others
+        for (int s = 0; s < ST; ++s)
+          if (s < nk) issue(stage_ptr(s), s, nt_c);
         __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
         lds_barrier();
-        if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST);
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+          __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+          lds_barrier();
+          if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST, nt_c);
+        }
       }
     }
+  };
+  if constexpr (kStreamB<BM, BN>) {
+    if (sole) go(std::true_type{});
+    else go(std::false_type{});
+  } else {
+    go(std::false_type{});
   }
 
   // ------------------------------------------------------------ epilogue

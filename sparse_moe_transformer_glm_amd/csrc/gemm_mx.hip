@@ -246,11 +246,13 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : s == 3 ? lds3
          : s == 4 ? lds4 : s == 5 ? lds5 : s == 6 ? lds6 : lds7;
   };
-  auto issue = [&](uint8_t* st, int kt) {
+  // NT: weight rows go with the non-temporal hint (a sole row tile, see kStreamB)
+  auto issue = [&](uint8_t* st, int kt, auto nt_c) {
+    constexpr bool NT = decltype(nt_c)::value;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int q = wave + i * NW;
-      if (kStreamB<BM, BN> && i * NW >= C::A_INST && sole)  // a weight-row copy
+      if (NT && i * NW >= C::A_INST)  // a weight-row copy
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
       else
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     for (int h = 0; h < 2; ++h) coff[sub][h] = ((4 * sub + 2 * h + lg) ^ sw) * 16;
   const int a_sc = C::SC_A + (wrow0 + lr) * 4, b_sc = C::SC_B + (wn * TN + lr) * 4;
 
-  auto run = [&](auto live_c) {
+  auto run = [&](auto live_c, auto nt_c) {
     constexpr int LIVE = decltype(live_c)::value;
     i32x8 fa[LIVE > 0 ? LIVE : 1], fb[FN];
     uint32_t sa[LIVE > 0 ? LIVE : 1], sb[FN];
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     };
 #pragma unroll
     for (int s = 0; s < ST; ++s)
-      if (s < nk) issue(stage_ptr(s), s);
+      if (s < nk) issue(stage_ptr(s), s, nt_c);
     if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS * (ST - 1)));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
           if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS * (ST - 2)));
           else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
           lds_barrier();
-          if (kt + ST < nk) issue(cur, kt + ST);
+          if (kt + ST < nk) issue(cur, kt + ST, nt_c);
         }
         if constexpr (LIVE > 0) mma(sub);
         // keep the next sub-step's fragment reads behind these MFMAs: one
@@ -359,12 +361,21 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
       });
     }
   };
-  switch (live_m) {
-    case 1: run(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (FM >= 2) run(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (FM >= 3) run(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr (FM >= 4) run(std::integral_constant<int, 4>{}); break;
-    default: run(std::integral_constant<int, 0>{}); break;  // DMA and barriers only
+  // the main loop, specialised on the live row blocks and the copy hint
+  auto go = [&](auto nt_c) {
+    switch (live_m) {
+      case 1: run(std::integral_constant<int, 1>{}, nt_c); break;
+      case 2: if constexpr (FM >= 2) run(std::integral_constant<int, 2>{}, nt_c); break;
+      case 3: if constexpr (FM >= 3) run(std::integral_constant<int, 3>{}, nt_c); break;
+      case 4: if constexpr (FM >= 4) run(std::integral_constant<int, 4>{}, nt_c); break;
+      default: run(std::integral_constant<int, 0>{}, nt_c); break;  // DMA and barriers only
+    }
+  };
+  if constexpr (kStreamB<BM, BN>) {
+    if (sole) go(std::true_type{});
+    else go(std::false_type{});
+  } else {
+    go(std::false_type{});
   }
 
   // ------------------------------------------------------------ epilogue
