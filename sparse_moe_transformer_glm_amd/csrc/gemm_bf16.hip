@@ -178,7 +178,10 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       if (NT && i * NW >= C::A_INST)  // a weight-row copy
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
-      else
+      // With two stages every wait drains the counter, so an activation copy
+      // whose rows all lie past the tile's valid rows can be left out (its LDS
+      // rows feed only MFMA rows that are never stored).
+      else if (ST > 2 || i * NW >= C::A_INST || q * RPI < rows)
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, 0);
     }
@@ -239,7 +242,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
 #pragma unroll
     for (int s = 0; s < ST; ++s)
       if (s < nk) issue(stage_ptr(s), s, nt_c);
-    if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
+    // (with two stages the copy count varies: drain)
+    if (ST > 2 && ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
     load_frags(stage_ptr(0), 0, 0);
