@@ -31,6 +31,11 @@ constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-ro
 #define GLM_XCD_BLOCK_ROUTED_GU 16
 #endif
 constexpr int kXcdBlock = GLM_XCD_BLOCK, kXcdBlockRoutedGu = GLM_XCD_BLOCK_ROUTED_GU;
+// Average rows per expert up to which the two-stage gate/up GEMM issues each
+// refill before its wait (GateUpArgs::early).
+#ifndef GLM_EARLY_MAX_ROWS
+#define GLM_EARLY_MAX_ROWS 192.0
+#endif
 
 // Cache policy of the weight-row copies.  The only row tile of a group is the
 // only reader of the group's weight rows in a launch, so on decode tiles (at
@@ -128,6 +133,7 @@ struct GateUpArgs {
   int T, D, E, F, Fs, k;
   int grid;                    // launched workgroups (>= desc_count, multiple of 8)
   int xblk;                    // XCD block of the tile mapping (xcd_tile)
+  int early;                   // two-stage tiles: issue each refill before the wait
 };
 // Tile shape of a grouped GEMM launch.  `wide` says the output width allows
 // the 256-column tiles (gate/up: F and F_shared multiples of 128; down and

@@ -75,7 +75,9 @@ __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
 
 
-template <class C, int MODE>
+// EARLY (two stages only): each stage's refill is issued before the wait for
+// the next stage instead of after it (see the main loop).
+template <class C, int MODE, bool EARLY>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, DownArgs dn) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::ST, MB = C::MB;
   constexpr int WN = C::WN, NW = C::NW, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
@@ -178,10 +180,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       if (NT && i * NW >= C::A_INST)  // a weight-row copy
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, kCpolNt);
-      // With two stages every wait drains the counter, so an activation copy
-      // whose rows all lie past the tile's valid rows can be left out (its LDS
-      // rows feed only MFMA rows that are never stored).
-      else if (ST > 2 || i * NW >= C::A_INST || q * RPI < rows)
+      else
         __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)kt * BK),
                                          (lds_void*)(st + q * (RPI * BK)), 16, 0, 0);
     }
@@ -204,6 +203,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     for (int n = 0; n < FN; ++n) acc[m][n] = acc_t{};
 
   const int nk = K / BK;
+  constexpr bool early = EARLY && ST == 2;
+  static_assert(!EARLY || ST == 2, "copy-before-wait order needs two stages");
 
   // Main loop, specialised on the number of live MFMA row blocks (LIVE) so the
   // inner loop has no branches.  Software pipeline per stage: reads of
@@ -242,8 +243,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
 #pragma unroll
     for (int s = 0; s < ST; ++s)
       if (s < nk) issue(stage_ptr(s), s, nt_c);
-    // (with two stages the copy count varies: drain)
-    if (ST > 2 && ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
+    if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
     load_frags(stage_ptr(0), 0, 0);
@@ -260,10 +260,24 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
           // kt+2 .. kt+ST-1 may stay in flight), meet the barrier, refill this
           // stage ST steps ahead and read the next stage's first fragments;
           // the MFMAs below then cover that read latency.
-          if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 2)));
-          else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
-          lds_barrier();
-          if (kt + ST < nk) issue(cur, kt + ST, nt_c);
+          if constexpr (early) {
+            // The refill of this stage goes out before the wait for the next
+            // one, so a copy is always in flight; a second barrier then tells
+            // every wave that all copies of stage kt+1 have landed.
+            lds_barrier();  // every wave is done reading stage kt
+            if (kt + 2 < nk) {
+              issue(cur, kt + 2, nt_c);
+              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW));  // this wave's copies of kt+1
+            } else {
+              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+            }
+            asm volatile("s_barrier" ::: "memory");
+          } else {
+            if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 2)));
+            else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+            lds_barrier();
+            if (kt + ST < nk) issue(cur, kt + ST, nt_c);
+          }
           load_frags(stage_ptr((s + 1) % ST), 0, 0);  // slot 0 is free: sub-step KSUB-2 used it
         }
         mma(sub & 1);
@@ -292,9 +306,20 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
         __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
         lds_barrier();
         for (int kt = 0; kt + 1 < nk; ++kt) {
-          __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
-          lds_barrier();
-          if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST, nt_c);
+          if constexpr (early) {  // the same two barriers per step as the other waves
+            lds_barrier();
+            if (kt + 2 < nk) {
+              issue(stage_ptr(kt % ST), kt + 2, nt_c);
+              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW));
+            } else {
+              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+            }
+            asm volatile("s_barrier" ::: "memory");
+          } else {
+            __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+            lds_barrier();
+            if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST, nt_c);
+          }
         }
       }
     }
@@ -481,7 +506,13 @@ using CfgNarrow = Cfg<32, 64, 64, 1, 2, 4, 16>;    // widths that are not a mult
 template <class C, int MODE>
 hipError_t launch_one(const GateUpArgs& gu, const DownArgs& dn, unsigned grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
-  grouped_gemm_kernel<C, MODE><<<grid, C::NT, 0, s>>>(gu, dn);
+  if constexpr (C::ST == 2 && MODE == GATE_UP) {
+    if (gu.early) {
+      grouped_gemm_kernel<C, MODE, true><<<grid, C::NT, 0, s>>>(gu, dn);
+      return hipGetLastError();
+    }
+  }
+  grouped_gemm_kernel<C, MODE, false><<<grid, C::NT, 0, s>>>(gu, dn);
   return hipGetLastError();
 }
 

@@ -358,6 +358,9 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     ga.H = at<bf16_t>(ws, P.H); ga.Hs = at<bf16_t>(ws, P.Hs);
     ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
     ga.xblk = (!P.dense && P.gu.BM == 256) ? kXcdBlockRoutedGu : kXcdBlock;
+    // Copy ahead of the wait on moderately filled 256-row tiles; at higher
+    // average fill the second stage in flight congests the L2 miss path.
+    ga.early = !P.dense && (double)P.T * P.k <= GLM_EARLY_MAX_ROWS * P.E;
     ga.grid = xcd_grid(P.gu_cap, ga.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
     GLM_HIP(launch_gateup_bf16(ga, P.gu, s));
