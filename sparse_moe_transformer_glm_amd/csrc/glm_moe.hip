@@ -330,7 +330,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     ga.H = at<uint8_t>(ws, P.H); ga.Hsc = at<uint8_t>(ws, P.Hsc);
     ga.Hs = at<uint8_t>(ws, P.Hs); ga.Hssc = at<uint8_t>(ws, P.Hssc);
     ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
-    ga.xblk = kXcdBlock;
+    ga.xblk = P.gu.BM == 256 ? kXcdBlockMxGu : kXcdBlock;
     ga.grid = xcd_grid(P.gu_cap, ga.xblk);
     GLM_HIP(launch_gateup_mx(ga, P.gu, s));
 
@@ -341,7 +341,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     da.sw2 = static_cast<const uint8_t*>(shared_w2); da.sw2s = W.sw2s;
     da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
-    da.xblk = kXcdBlock;
+    da.xblk = P.dn.BM == 256 ? kXcdBlockMxDn : kXcdBlock;
     da.grid = xcd_grid(P.dn_cap, da.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
     GLM_HIP(launch_down_mx(da, P.dn, s));
