@@ -157,7 +157,7 @@ struct DownArgs {
   const bf16_t* w2;            // [E][D][F]
   const bf16_t* sw2;           // [D][Fs]
   const float* row_w;          // [T*k] routing weight of each expert-sorted row
-  const TileDesc* desc;        // routed groups, then the shared expert (group E)
+  const TileDesc* desc;        // tiles of the routed groups and the shared expert (group E)
   const int32_t* desc_count;
   float* Y;                    // [T][k+1][D]: slot j < k routed (weighted), slot k shared
   int T, D, E, F, Fs, k;

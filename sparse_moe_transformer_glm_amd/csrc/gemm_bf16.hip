@@ -11,7 +11,10 @@
 // work, and each wave waits only for the oldest stage (vmcnt), so HBM latency
 // is covered by up to ST-1 steps of math.  Rows are stored unpadded with the
 // 16-byte chunks of each row XOR-swizzled, which keeps the MFMA fragment reads
-// free of bank conflicts.
+// free of bank conflicts.  With two stages the copy-first variant (EARLY)
+// refills a stage before waiting for the next one.  A tile that is the only
+// row tile of its group copies the group's weight rows with the non-temporal
+// hint on tiles of up to GLM_STREAM_B_MAX_BM rows (it is their only reader).
 //
 // Math: each wave owns a (BM/WM) x (BN/WN) sub-tile and accumulates it with
 // v_mfma_f32_32x32x16_bf16 (MB = 32) or v_mfma_f32_16x16x32_bf16 (MB = 16).
@@ -25,7 +28,8 @@
 //    of the PocketLLM "GLM-5.2" page, Implemented execution path).
 //  * DOWN: Y[t][j] = w[t][j] * (H W2^T): the routing weight is applied and the
 //    row lands in its (token, slot) place (un-permute); no atomics.  The
-//    shared expert is the last group and writes Y[t][k] with weight 1.
+//    shared expert is group E and writes Y[t][k] with weight 1.  Slot rows are
+//    written with non-temporal stores (each is read once, by the combine).
 // A streaming kernel then forms out[t] = Y[t][k] + sum_j Y[t][j] in slot
 // order: the always-on shared expert merged with the weighted routed outputs
 // (GLM-5.2 anatomy page, Mixture of Experts panel).

@@ -152,7 +152,7 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
               : gemm_shape(per_group, wide_gu && !few_tiles);
     P.dn = mx ? gemm_shape_mx(per_group, P.D % 256 == 0 && !few_tiles)
               : gemm_shape(per_group, P.D % 256 == 0 && !few_tiles);
-    // routed tiles, then the shared (or dense) group's tiles (group E)
+    // tile-list capacity: routed tiles plus the shared (or dense) group's (group E)
     P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) +
                cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
     P.dn_cap = (dense ? 0 : desc_cap(A, P.E, P.dn, P.D / P.dn.BN)) +
