@@ -238,14 +238,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int g = s_og[lo];
     const int rows = g < E ? s_cnt[g] : p.T;
     const int mt = cdiv(rows, p.gu.BM);
-    int nt, m;
-    tile_order(i - s_pg[lo], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
+    int nt, m, r0, rt;
+    if (mt == 1 && g < E) {  // one row tile (the common case): no divisions
+      m = 0;
+      nt = i - s_pg[lo];
+      r0 = 0;
+      rt = rows;
+    } else {
+      tile_order(i - s_pg[lo], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
+      const int gran = min(64, p.gu.BM);
+      r0 = tile_row0(m, mt, rows, gran);
+      rt = tile_row0(m + 1, mt, rows, gran) - r0;
+    }
     TileDesc d;
     d.group = g | (mt == 1 ? kSoleRowTile : 0);
-    const int gran = min(64, p.gu.BM);
-    const int r0 = tile_row0(m, mt, rows, gran);
     d.row0 = (g < E ? s_off[g] : 0) + r0;
-    d.rows = tile_row0(m + 1, mt, rows, gran) - r0;
+    d.rows = rt;
     d.col0 = nt * (p.gu.BN / 2);
     gu_desc[i] = d;
   }
@@ -259,14 +267,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int g = s_od[lo];
     const int grows = g < E ? s_cnt[g] : p.T;
     const int mt = cdiv(grows, p.dn.BM);
-    int nt, m;
-    tile_order(i - s_pd[lo], mt, p.D / p.dn.BN, g == E, &m, &nt);
+    int nt, m, r0, rt;
+    if (mt == 1 && g < E) {
+      m = 0;
+      nt = i - s_pd[lo];
+      r0 = 0;
+      rt = grows;
+    } else {
+      tile_order(i - s_pd[lo], mt, p.D / p.dn.BN, g == E, &m, &nt);
+      const int gran = min(64, p.dn.BM);
+      r0 = tile_row0(m, mt, grows, gran);
+      rt = tile_row0(m + 1, mt, grows, gran) - r0;
+    }
     TileDesc d;
     d.group = g | (mt == 1 ? kSoleRowTile : 0);
-    const int gran = min(64, p.dn.BM);
-    const int r0 = tile_row0(m, mt, grows, gran);
     d.row0 = (g < E ? s_off[g] : 0) + r0;
-    d.rows = tile_row0(m + 1, mt, grows, gran) - r0;
+    d.rows = rt;
     d.col0 = nt * p.dn.BN;
     dn_desc[i] = d;
   }
