@@ -23,8 +23,9 @@ constexpr int kTokTile = 64;   // tokens per routing tile (one bit per token in 
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
 // Consecutive logical tiles kept on one XCD (see xcd_tile): kXcdBlock in
 // general; on 256-row tiles, kXcdBlockRoutedGu for the bf16 gate/up GEMM of
-// routed experts and kXcdBlockMxGu / kXcdBlockMxDn for the MXFP8 GEMMs
-// (measured per launch kind).
+// routed experts and kXcdBlockMxGu / kXcdBlockMxDn for the MXFP8 GEMMs; on
+// 32-row (decode) tiles kXcdBlockDecodeDn for the bf16 down GEMM (measured
+// per launch kind).
 #ifndef GLM_XCD_BLOCK
 #define GLM_XCD_BLOCK 64
 #endif
@@ -39,6 +40,10 @@ constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-ro
 #endif
 constexpr int kXcdBlock = GLM_XCD_BLOCK, kXcdBlockRoutedGu = GLM_XCD_BLOCK_ROUTED_GU;
 constexpr int kXcdBlockMxGu = GLM_XCD_BLOCK_MX_GU, kXcdBlockMxDn = GLM_XCD_BLOCK_MX_DN;
+#ifndef GLM_XCD_BLOCK_DECODE_DN
+#define GLM_XCD_BLOCK_DECODE_DN 128
+#endif
+constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
 // Average rows per expert up to which the two-stage gate/up GEMM issues each
 // refill before its wait (GateUpArgs::early).
 #ifndef GLM_EARLY_MAX_ROWS
