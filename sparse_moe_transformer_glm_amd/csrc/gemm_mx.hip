@@ -524,11 +524,13 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
 // 256 x 128: at one byte per element it moves fewer bytes per flop than the
 // bf16 256 x 256 tile, and its 64 accumulator registers per wave leave room
 // for a third stage.
+// The decode tile keeps two stages (76 KB of LDS), so two workgroups share a
+// CU and one's tile setup and first copies overlap the other's weight stream.
 #ifndef GLM_MX_CFG_BIG
 #define GLM_MX_CFG_BIG 256, 128, 4, 2, 3
 #endif
 #ifndef GLM_MX_CFG_DECODE
-#define GLM_MX_CFG_DECODE 32, 256, 1, 4, 4
+#define GLM_MX_CFG_DECODE 32, 256, 1, 4, 2
 #endif
 using MxDecode = Cfg<GLM_MX_CFG_DECODE>;
 #ifndef GLM_MX_CFG_MID
