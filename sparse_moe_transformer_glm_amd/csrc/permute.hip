@@ -49,6 +49,56 @@ __device__ inline int tile_row0(int m, int mt, int rows, int gran) {
   return min(rows, (int)(((long long)m * units) / mt) * gran);
 }
 
+// Tile descriptors of one GEMM, positions [0, total).  Listing position lo
+// (0..E) holds group og[lo], whose tiles start at position pos[lo]; pos is
+// non-decreasing and groups without tiles repeat the next group's position.
+// Wave w writes a contiguous chunk of positions, 64 consecutive ones per round
+// (coalesced 16-byte stores).  One binary search finds the group of the chunk's
+// first position; after that each lane steps forward from the group of the
+// previous round's last position, a few LDS reads per round.
+__device__ inline void write_descs(const int* pos, const int* og, int total, const int* cnt,
+                                   const int* off, int T, int E, int BM, int shared_nt,
+                                   int col_w, TileDesc* __restrict__ out) {
+  constexpr int kWaves = kScanThreads / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int chunk = cdiv(cdiv(total, kWaves), kWave) * kWave;
+  const int b0 = wave * chunk, b1 = min(total, b0 + chunk);
+  if (b0 >= b1) return;
+  int lo = 0, hi = E;  // largest position with pos <= b0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pos[mid] <= b0) lo = mid; else hi = mid - 1;
+  }
+  for (int base = b0; base < b1; base += kWave) {
+    const int i = base + lane;
+    int l = lo;
+    while (l < E && pos[l + 1] <= i) ++l;
+    lo = __shfl(l, kWave - 1, kWave);
+    if (i >= b1) continue;
+    const int g = og[l];
+    const int rows = g < E ? cnt[g] : T;
+    const int mt = cdiv(rows, BM);
+    int nt, m, r0, rt;
+    if (mt == 1 && g < E) {  // one row tile (the common case): no divisions
+      m = 0;
+      nt = i - pos[l];
+      r0 = 0;
+      rt = rows;
+    } else {
+      tile_order(i - pos[l], mt, shared_nt, g == E, &m, &nt);
+      const int gran = min(64, BM);
+      r0 = tile_row0(m, mt, rows, gran);
+      rt = tile_row0(m + 1, mt, rows, gran) - r0;
+    }
+    TileDesc d;
+    d.group = g | (mt == 1 ? kSoleRowTile : 0);
+    d.row0 = (g < E ? off[g] : 0) + r0;
+    d.rows = rt;
+    d.col0 = nt * col_w;
+    out[i] = d;
+  }
+}
+
 // Single workgroup.  masks[tile][e] has bit i set when token tile*64+i chose e.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const uint64_t* __restrict__ masks, ScanParams p, int32_t* __restrict__ counts,
@@ -228,64 +278,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __syncthreads();
 
   // tile descriptors: groups in listing order, then output-column tile, then row tile
-  const int gu_total = s_gu[E + 1];
-  for (int i = tid; i < gu_total; i += kScanThreads) {
-    int lo = 0, hi = E;  // largest position with s_pg <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pg[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int g = s_og[lo];
-    const int rows = g < E ? s_cnt[g] : p.T;
-    const int mt = cdiv(rows, p.gu.BM);
-    int nt, m, r0, rt;
-    if (mt == 1 && g < E) {  // one row tile (the common case): no divisions
-      m = 0;
-      nt = i - s_pg[lo];
-      r0 = 0;
-      rt = rows;
-    } else {
-      tile_order(i - s_pg[lo], mt, 2 * p.Fs / p.gu.BN, g == E, &m, &nt);
-      const int gran = min(64, p.gu.BM);
-      r0 = tile_row0(m, mt, rows, gran);
-      rt = tile_row0(m + 1, mt, rows, gran) - r0;
-    }
-    TileDesc d;
-    d.group = g | (mt == 1 ? kSoleRowTile : 0);
-    d.row0 = (g < E ? s_off[g] : 0) + r0;
-    d.rows = rt;
-    d.col0 = nt * (p.gu.BN / 2);
-    gu_desc[i] = d;
-  }
-  const int dn_total = s_dn[E + 1];
-  for (int i = tid; i < dn_total; i += kScanThreads) {
-    int lo = 0, hi = E;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pd[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int g = s_od[lo];
-    const int grows = g < E ? s_cnt[g] : p.T;
-    const int mt = cdiv(grows, p.dn.BM);
-    int nt, m, r0, rt;
-    if (mt == 1 && g < E) {
-      m = 0;
-      nt = i - s_pd[lo];
-      r0 = 0;
-      rt = grows;
-    } else {
-      tile_order(i - s_pd[lo], mt, p.D / p.dn.BN, g == E, &m, &nt);
-      const int gran = min(64, p.dn.BM);
-      r0 = tile_row0(m, mt, grows, gran);
-      rt = tile_row0(m + 1, mt, grows, gran) - r0;
-    }
-    TileDesc d;
-    d.group = g | (mt == 1 ? kSoleRowTile : 0);
-    d.row0 = (g < E ? s_off[g] : 0) + r0;
-    d.rows = rt;
-    d.col0 = nt * p.dn.BN;
-    dn_desc[i] = d;
-  }
+  write_descs(s_pg, s_og, s_gu[E + 1], s_cnt, s_off, p.T, E, p.gu.BM, 2 * p.Fs / p.gu.BN,
+              p.gu.BN / 2, gu_desc);
+  write_descs(s_pd, s_od, s_dn[E + 1], s_cnt, s_off, p.T, E, p.dn.BM, p.D / p.dn.BN, p.dn.BN,
+              dn_desc);
 }
 
 // One wave per 64-token tile.  A token's rank among the tile's tokens of
