@@ -284,6 +284,9 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
           }
           load_frags(stage_ptr((s + 1) % ST), 0, 0);  // slot 0 is free: sub-step KSUB-2 used it
         }
+        // Pin the reads issued above ahead of this sub-step's MFMAs: left free,
+        // the scheduler sinks each read to its first MFMA and waits at once.
+        __builtin_amdgcn_sched_barrier(0);
         mma(sub & 1);
       }
     };
