@@ -44,8 +44,8 @@ constexpr int kXcdBlockMxGu = GLM_XCD_BLOCK_MX_GU, kXcdBlockMxDn = GLM_XCD_BLOCK
 #define GLM_XCD_BLOCK_DECODE_DN 128
 #endif
 constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
-// Average rows per expert up to which the two-stage gate/up GEMM issues each
-// refill before its wait (GateUpArgs::early).
+// Average rows per expert up to which the two-stage gate/up and down GEMMs
+// issue each refill before their wait (GateUpArgs::early, DownArgs::early).
 #ifndef GLM_EARLY_MAX_ROWS
 #define GLM_EARLY_MAX_ROWS 192.0
 #endif
@@ -168,6 +168,7 @@ struct DownArgs {
   int T, D, E, F, Fs, k;
   int grid;
   int xblk;
+  int early;                   // two-stage tiles: issue each refill before the wait
 };
 hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s);
 

@@ -513,8 +513,8 @@ using CfgNarrow = Cfg<32, 64, 64, 1, 2, 4, 16>;    // widths that are not a mult
 template <class C, int MODE>
 hipError_t launch_one(const GateUpArgs& gu, const DownArgs& dn, unsigned grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
-  if constexpr (C::ST == 2 && MODE == GATE_UP) {
-    if (gu.early) {
+  if constexpr (C::ST == 2) {
+    if (MODE == GATE_UP ? gu.early : dn.early) {
       grouped_gemm_kernel<C, MODE, true><<<grid, C::NT, 0, s>>>(gu, dn);
       return hipGetLastError();
     }

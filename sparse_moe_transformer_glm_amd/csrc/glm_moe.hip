@@ -371,6 +371,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
     da.xblk = P.dn.BM == 32 ? kXcdBlockDecodeDn : kXcdBlock;
+    da.early = ga.early;  // same two-stage ring, same fill rule
     da.grid = xcd_grid(P.dn_cap, da.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));
     GLM_HIP(launch_down_bf16(da, P.dn, s));
