@@ -90,6 +90,10 @@ SMALL = {
     "mid_rows": W(name="mid_rows", T=600, D=256, E=32, k=2, F=128, Fs=64, seed=17,
                   weight_seed=17),
     "top32": W(name="top32", T=50, D=128, E=64, k=32, F=64, Fs=64, seed=18, weight_seed=18),
+    # ~160 rows per expert: 256-row tiles with the copy-before-wait hand-over
+    # in both grouped GEMMs, every output element compared
+    "early_rows": W(name="early_rows", T=640, D=256, E=8, k=2, F=128, Fs=128, seed=21,
+                    weight_seed=21),
     "f32_ragged": W("tiny_f32", name="f32_ragged", T=37, D=100, E=5, k=2, F=30, Fs=7, seed=19,
                     weight_seed=19),
     "f32_many": W("tiny_f32", name="f32_many", T=300, D=64, E=16, k=4, F=32, Fs=48, seed=20,
