@@ -77,6 +77,15 @@ typedef struct {
  * would reject.  T = 0 yields 0 bytes. */
 GLM_MOE_API int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes);
 
+/* The same size as a return value, the form of the boundary's plain
+ * statement: bytes of workspace glm_moe_route / glm_moe_forward need for `d`
+ * and `top_k`.  Host-only; enqueues nothing.  Returns 0 when T = 0 (no
+ * workspace needed; glm_moe_last_error() is then empty) and 0 for dims that
+ * route/forward would reject (glm_moe_last_error() names the cause; use
+ * glm_moe_workspace_size for the status code).  Any valid call with T > 0
+ * needs a non-zero workspace. */
+GLM_MOE_API size_t glm_moe_workspace_bytes(const glm_moe_dims* d, int top_k);
+
 /* Router only: steps "sigmoid router scores", "correction bias affects top-k
  * selection", "un-biased selected scores renormalised and scaled" of the layer
  * statement (GLM-5.2 anatomy page, Mixture of Experts panel).
@@ -230,8 +239,8 @@ GLM_MOE_API int glm_moe_dense_ffn(const glm_moe_dims* d, const glm_moe_options* 
  *   w2 [E][D][F] codes, w2_scale [E][F/128][D][4];
  *   shared_w1, shared_w3 [F_shared][D], scales [D/128][F_shared][4];
  *   shared_w2 [D][F_shared], scale [F_shared/128][D][4].
- * The pages name FP8 GLM-5.2 artifacts (frontier-model-atlas "GLM-5.2 model
- * anatomy", release panel) without their scaling; this block format is the
+ * The pages name BF16/FP8 GLM-5.2 artifacts ("Inside GLM" course page,
+ * Release anatomy lesson) without their scaling; this block format is the
  * one gfx950 applies inside its FP8 MFMA. */
 typedef struct {
   const void* w1; const void* w1_scale;

@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY (same import rule as ``oracle.moe``).
 
-The pages name FP8 GLM-5.2 artifacts (frontier-model-atlas "GLM-5.2 model
-anatomy", release / artifacts panel) but no scaling format.  The format here is
+The pages name BF16/FP8 GLM-5.2 artifacts ("Inside GLM" course page,
+Release anatomy lesson) but no scaling format.  The format here is
 the OCP Microscaling (MX) v1.0 MXFP8 format, written out from its definition:
 
 * element: FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa

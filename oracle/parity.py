@@ -133,23 +133,20 @@ BF16_MAX_REL = 2e-2
 BF16_MEAN_REL = 2e-3
 F32_MAX_REL = 1e-5
 WEIGHT_TOL = 1e-5
-# MXFP8 layer against oracle.forward_mx, which performs the same quantisations:
-# differences come from the accumulation precision of the FP8 MFMA and from
-# the hidden values it moves across an E4M3 rounding decision (see mx_explain).
-MX_MEAN_REL = 2e-3   # mean |diff| / rms over all outputs, before explanation
-# explained flips per hidden value, at most: the MFMA's accumulation error
-# (typically 2^-19, at most about 2^-14 of the term sum) moves 0.1-0.4% of the
-# E4M3 decisions of the hidden values on the test layers (GLM shape included)
-MX_FLIP_FRAC = 1e-2
+# The MXFP8 layer is held to the bf16 bounds above against oracle.forward_mx,
+# which performs the same quantisations.
 
 
 # ------------------------------------------------------ MXFP8 rounding ties
 
 # Error budget of an MXFP8 dot product computed by the block-scaled FP8 MFMA,
-# relative to the sum of the magnitudes of its terms.  The MFMA sums each
-# 64-element step with limited internal precision: on gfx950 the error of one
-# step reached 1.7e-5 of that sum, and 6.1e-5 over a 512-long product, for
-# identical inputs; 2^-13 (1.2e-4) is the budget used here.
+# relative to the sum of the magnitudes of its terms, for the diagnostic
+# below.  It was measured on the GPU, not derived: the MFMA sums each
+# 64-element step with limited internal precision, and on gfx950 the error of
+# one step reached 1.7e-5 of that sum, and 6.1e-5 over a 512-long product, for
+# identical inputs; 2^-13 (1.2e-4) is the budget used here.  Because it comes
+# from the hardware under test, mx_explain is a diagnostic and never the
+# pass condition of a parity test.
 MX_HW_REL = 2.0 ** -13
 
 

@@ -7,10 +7,10 @@ binding.  Build the library with ``python -m sparse_moe_transformer_glm_amd.buil
 from ._lib import (BF16, EHIP, EINVAL, EUNSUPPORTED, EWORKSPACE, F32, LIB_PATH, MXFP8, OK,
                    STAGES, GlmMoeError, MxWeights, Options, Trace, dense_ffn, dense_workspace_size,
                    forward, forward_mx, lib, new_workspace, options, pack_mx_scales, route,
-                   workspace_size)
+                   workspace_bytes, workspace_size)
 
 __all__ = ["BF16", "EHIP", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "F32", "LIB_PATH", "MXFP8",
            "OK", "STAGES", "GlmMoeError", "MxWeights", "Options", "Trace", "dense_ffn",
            "dense_workspace_size", "forward", "forward_mx", "lib", "new_workspace", "options",
            "pack_mx_scales",
-           "route", "workspace_size"]
+           "route", "workspace_bytes", "workspace_size"]

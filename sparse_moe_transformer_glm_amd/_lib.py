@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         pd, po = ctypes.POINTER(Dims), ctypes.POINTER(Options)
         L.glm_moe_workspace_size.argtypes = [pd, i32, ctypes.POINTER(sz)]
         L.glm_moe_workspace_size_ex.argtypes = [pd, po, i32, ctypes.POINTER(sz)]
+        L.glm_moe_workspace_bytes.argtypes = [pd, i32]
+        L.glm_moe_workspace_bytes.restype = sz
         L.glm_moe_route.argtypes = [pd, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.glm_moe_route_ex.argtypes = [pd, po, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.glm_moe_forward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
@@ -136,6 +138,17 @@ def workspace_size(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
                                            None if opts is None else ctypes.byref(opts), top_k,
                                            ctypes.byref(n)), "glm_moe_workspace_size_ex")
     return n.value
+
+
+def workspace_bytes(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
+                    dtype: torch.dtype = torch.bfloat16) -> int:
+    """``glm_moe_workspace_bytes``: workspace of the plain route/forward calls
+    (0 for T = 0; raises on dims those calls would reject)."""
+    L = lib()
+    n = L.glm_moe_workspace_bytes(ctypes.byref(dims(T, D, E, F, Fs, dtype)), top_k)
+    if n == 0 and T > 0:
+        raise GlmMoeError(EINVAL, "glm_moe_workspace_bytes", L.glm_moe_last_error().decode())
+    return int(n)
 
 
 def dense_workspace_size(T: int, D: int, F: int, dtype: torch.dtype = torch.bfloat16,

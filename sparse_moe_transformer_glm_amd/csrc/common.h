@@ -46,8 +46,10 @@ constexpr int kXcdBlockMxGu = GLM_XCD_BLOCK_MX_GU, kXcdBlockMxDn = GLM_XCD_BLOCK
 constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
 // Average rows per expert up to which the two-stage gate/up and down GEMMs
 // issue each refill before their wait (GateUpArgs::early, DownArgs::early).
+// Measured: the two orders are equal at 160 rows per expert, the plain order
+// is faster at 192.
 #ifndef GLM_EARLY_MAX_ROWS
-#define GLM_EARLY_MAX_ROWS 192.0
+#define GLM_EARLY_MAX_ROWS 160.0
 #endif
 
 // Cache policy of the weight-row copies.  The only row tile of a group is the

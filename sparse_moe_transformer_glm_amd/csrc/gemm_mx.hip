@@ -2,8 +2,8 @@
 // block-scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
 //
 // Format: OCP MX with E4M3 elements and one E8M0 scale per 32 consecutive
-// elements along the contraction dimension.  The pages name FP8 GLM-5.2
-// artifacts (frontier-model-atlas "GLM-5.2 model anatomy", release panel) but
+// elements along the contraction dimension.  The pages name BF16/FP8 GLM-5.2
+// artifacts ("Inside GLM" course page, Release anatomy lesson) but
 // not their scaling; MX is the format this hardware scales inside the MFMA.
 //
 // Same data flow as the bf16 kernels: C[M x N] = A[M x K] . B[N x K]^T, both

@@ -447,6 +447,13 @@ int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes) {
   return glm_moe_workspace_size_ex(d, nullptr, top_k, bytes);
 }
 
+size_t glm_moe_workspace_bytes(const glm_moe_dims* d, int top_k) {
+  g_err[0] = 0;
+  size_t n = 0;
+  if (glm_moe_workspace_size_ex(d, nullptr, top_k, &n) != GLM_MOE_OK) return 0;
+  return n;
+}
+
 int glm_moe_route_ex(const glm_moe_dims* d, const glm_moe_options* opts, const void* x,
                      const float* router_w, const float* corr_bias, int top_k, float scale,
                      int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,

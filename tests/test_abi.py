@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("glm_moe_route", "glm_moe_forward", "glm_moe_workspace_size",
-              "glm_moe_status_string"):
+    for n in ("glm_moe_route", "glm_moe_forward", "glm_moe_workspace_bytes",
+              "glm_moe_workspace_size", "glm_moe_status_string"):
         assert n in names
 
 
@@ -59,6 +59,31 @@ def _ws(T, D, E, F, Fs, k, dt=glm.BF16):
     st = glm.lib().glm_moe_workspace_size(ctypes.byref(Dims(T, D, E, F, Fs, dt, dt)), k,
                                           ctypes.byref(n))
     return st, n.value
+
+
+def test_workspace_bytes_matches_workspace_size():
+    """glm_moe_workspace_bytes returns the size glm_moe_workspace_size writes,
+    0 with an empty error for T = 0, and 0 with the cause for rejected dims."""
+    L = glm.lib()
+    for T, D, E, F, Fs, k, dt in ((64, 6144, 256, 2048, 2048, 8, glm.BF16),
+                                  (8192, 6144, 256, 2048, 2048, 8, glm.BF16),
+                                  (37, 100, 5, 30, 7, 2, glm.F32), (1, 64, 4, 64, 64, 1, glm.BF16)):
+        d = Dims(T, D, E, F, Fs, dt, dt)
+        n = ctypes.c_size_t(0)
+        assert L.glm_moe_workspace_size(ctypes.byref(d), k, ctypes.byref(n)) == glm.OK
+        assert L.glm_moe_workspace_bytes(ctypes.byref(d), k) == n.value > 0
+    assert L.glm_moe_workspace_bytes(ctypes.byref(Dims(0, 128, 8, 64, 64, glm.BF16, glm.BF16)),
+                                     2) == 0
+    assert L.glm_moe_last_error() == b""
+    for d, k in ((Dims(64, 128, 8, 64, 64, glm.BF16, glm.BF16), 9),     # top_k > E
+                 (Dims(64, 128, 300, 64, 64, glm.BF16, glm.BF16), 8),   # E > 256
+                 (Dims(64, 100, 8, 64, 64, glm.BF16, glm.BF16), 2)):    # D not /64 on bf16
+        assert L.glm_moe_workspace_bytes(ctypes.byref(d), k) == 0
+        assert L.glm_moe_last_error() != b""
+    assert L.glm_moe_workspace_bytes(None, 2) == 0
+    assert glm.workspace_bytes(64, 128, 8, 64, 64, 2) == glm.workspace_size(64, 128, 8, 64, 64, 2)
+    with pytest.raises(glm.GlmMoeError):
+        glm.workspace_bytes(64, 128, 8, 64, 64, 9)
 
 
 def test_workspace_sizes():

@@ -14,6 +14,7 @@ import oracle
 from oracle import parity
 import workloads as wl
 from workloads.device import stream_layer, to_device, upload_layer
+from expert_feed import ExpertFeed
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +55,15 @@ def check(L, out, idx, wt, k=None, scale=None, sample=None, label="", ref=None):
     assert rep.ok, f"{label}: invalid routing on tokens {rep.invalid[:10]}"
     assert rep.max_weight_err <= parity.WEIGHT_TOL, f"{label}: weight err {rep.max_weight_err}"
     toks = np.arange(out.shape[0]) if sample is None else np.asarray(sample)
-    ref, _ = oracle.forward(L.x[toks], L.router_w, L.corr_bias,
-                            lambda e: (L.w1[e], L.w3[e], L.w2[e]), (L.sw1, L.sw3, L.sw2),
-                            k, scale, force_idx=rep.forced_idx[toks])
+    get = lambda e: (L.w1[e], L.w3[e], L.w2[e])
+    feed = ExpertFeed(get, np.unique(rep.forced_idx[toks])) if L.w.E * L.w.F * L.w.D > 1 << 30 \
+        else get
+    try:
+        ref, _ = oracle.forward(L.x[toks], L.router_w, L.corr_bias, feed, (L.sw1, L.sw3, L.sw2),
+                                k, scale, force_idx=rep.forced_idx[toks])
+    finally:
+        if feed is not get:
+            feed.close()
     o = parity.compare_output(out[toks], ref)
     log(f"{label}: tokens={rep.tokens} exact={rep.exact} near-tie={rep.excused} "
         f"max|dw|={rep.max_weight_err:.2e} out max/rms={o.max_rel:.3e} mean/rms={o.mean_rel:.3e} "
@@ -91,8 +98,10 @@ SMALL = {
                   weight_seed=17),
     "top32": W(name="top32", T=50, D=128, E=64, k=32, F=64, Fs=64, seed=18, weight_seed=18),
     # ~160 rows per expert: 256-row tiles with the copy-before-wait hand-over
-    # in both grouped GEMMs, every output element compared
-    "early_rows": W(name="early_rows", T=640, D=256, E=8, k=2, F=128, Fs=128, seed=21,
+    # in both grouped GEMMs (gate/up K = 256, down K = 256: four K steps each,
+    # so both run the refill-then-wait order and its tail), every output
+    # element compared
+    "early_rows": W(name="early_rows", T=640, D=256, E=8, k=2, F=256, Fs=256, seed=21,
                     weight_seed=21),
     "f32_ragged": W("tiny_f32", name="f32_ragged", T=37, D=100, E=5, k=2, F=30, Fs=7, seed=19,
                     weight_seed=19),
@@ -121,6 +130,48 @@ def test_route_entry_matches_forward_routing():
                                  L.corr_bias, L.w.k, L.w.scale)
     assert rep.ok and rep.max_weight_err <= parity.WEIGHT_TOL
     assert rep.weight_sum_err <= 2e-6
+
+
+def test_plain_entry_points_through_ctypes():
+    """glm_moe_route and glm_moe_forward themselves (no options, no trace),
+    with the workspace sized by glm_moe_workspace_bytes, against the oracle."""
+    import ctypes
+    from sparse_moe_transformer_glm_amd._lib import Dims
+
+    w = wl.WORKLOADS["mid_bf16"]
+    L = wl.make_layer(w, threads=4)
+    dev = upload_layer(L)
+    lib = glm.lib()
+    d = Dims(w.T, w.D, w.E, w.F, w.Fs, glm.BF16, glm.BF16)
+    n = lib.glm_moe_workspace_bytes(ctypes.byref(d), w.k)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    x, rw, cb, w1, w3, w2, sw1, sw3, sw2 = (t.data_ptr() for t in dev.args())
+
+    def fresh():
+        return (torch.full((w.T, w.k), -1, dtype=torch.int32, device="cuda"),
+                torch.full((w.T, w.k), float("nan"), dtype=torch.float32, device="cuda"),
+                torch.full((w.T, w.D), float("nan"), dtype=torch.float32, device="cuda"))
+
+    ridx, rwt, _ = fresh()
+    st = lib.glm_moe_route(ctypes.byref(d), x, rw, cb, w.k, w.scale, ridx.data_ptr(),
+                           rwt.data_ptr(), ws.data_ptr(), n, s)
+    assert st == glm.OK, lib.glm_moe_last_error()
+    idx, wt, out = fresh()
+    st = lib.glm_moe_forward(ctypes.byref(d), x, rw, cb, w1, w3, w2, sw1, sw3, sw2, w.k, w.scale,
+                             out.data_ptr(), idx.data_ptr(), wt.data_ptr(), ws.data_ptr(), n, s)
+    assert st == glm.OK, lib.glm_moe_last_error()
+    _, _, out_noroute = fresh()  # routing outputs are nullable
+    st = lib.glm_moe_forward(ctypes.byref(d), x, rw, cb, w1, w3, w2, sw1, sw3, sw2, w.k, w.scale,
+                             out_noroute.data_ptr(), None, None, ws.data_ptr(), n, s)
+    assert st == glm.OK, lib.glm_moe_last_error()
+    torch.cuda.synchronize()
+    out, idx, wt = out.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy()
+    np.testing.assert_array_equal(ridx.cpu().numpy(), idx)
+    np.testing.assert_array_equal(rwt.cpu().numpy(), wt)
+    np.testing.assert_array_equal(out_noroute.cpu().numpy(), out)
+    check(L, out, idx, wt, label="plain entry points")
 
 
 def test_weights_sum_to_scale_and_k1_exact():
@@ -282,9 +333,9 @@ def _sample(T, n, extra=()):
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,n_sample", [("glm_decode", None), ("glm_prefill", 24),
-                                           ("glm_chunk_2k", 16), ("glm_skew", 16),
-                                           ("glm_skew_mild", 16)])
+@pytest.mark.parametrize("name,n_sample", [("glm_decode", None), ("glm_prefill", 1024),
+                                           ("glm_chunk_2k", 1024), ("glm_skew", 1024),
+                                           ("glm_skew_mild", 1024)])
 def test_glm_shape(glm_layer, name, n_sample):
     L, dev = _glm_case(glm_layer, name)
     t0 = time.time()

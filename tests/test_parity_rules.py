@@ -109,6 +109,29 @@ def test_group_near_tie_swap_is_excused():
 from oracle import mx  # noqa: E402
 
 
+def test_compare_output_hand_values():
+    """max and mean |out - ref| relative to rms(ref), on values worked by hand.
+
+    ref = [[3, -4], [0, 0]]: rms = sqrt((9 + 16) / 4) = 2.5.  out differs by
+    +0.5 at (0, 0) and -0.25 at (1, 1): max 0.5 / 2.5 = 0.2, mean
+    0.75 / 4 / 2.5 = 0.075 (the sign of a difference does not matter).
+    """
+    ref = np.array([[3.0, -4.0], [0.0, 0.0]])
+    out = np.array([[3.5, -4.0], [0.0, -0.25]])
+    o = parity.compare_output(out, ref)
+    assert o.rms == 2.5
+    assert o.max_rel == 0.2
+    assert o.mean_rel == 0.075
+    # swapping the roles changes the rms (out is not the reference)
+    assert parity.compare_output(ref, out).rms != 2.5
+    # an all-zero reference: differences are absolute
+    z = parity.compare_output(np.array([0.5, -1.0]), np.zeros(2))
+    assert (z.rms, z.max_rel, z.mean_rel) == (1.0, 1.0, 0.75)
+    # float32 inputs are compared in float64
+    o32 = parity.compare_output(out.astype(np.float32), ref.astype(np.float32))
+    assert (o32.max_rel, o32.mean_rel) == (0.2, 0.075)
+
+
 def _mx_layer(seed=9, T=48, D=256, E=8, F=128, k=2):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, D))
