@@ -269,6 +269,25 @@ GLM_MOE_API int glm_moe_forward_mx(const glm_moe_dims* d, const glm_moe_options*
                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
                                    glm_moe_trace* trace);
 
+/* Where a forward call leaves the gated hidden rows in its workspace, for
+ * inspection (a test can read back the hidden values the kernels computed
+ * and quantised).  Byte offsets into the workspace of a call with the same
+ * dims, options and top_k; valid after that call has completed, until the
+ * workspace is reused.  bf16 layers hold bf16 hidden values, MXFP8 layers
+ * E4M3 codes with E8M0 scales (fp32 layers keep fp32 values):
+ *   row_assign   int32 [T*top_k]: expert-sorted row r holds assignment
+ *                row_assign[r] = t*top_k + j (token t, slot j)
+ *   hidden       [T*top_k][F]   rows in expert-sorted order
+ *   hidden_scale [F/128][T*top_k][4]  (MXFP8 only; else 0)
+ *   shared_hidden       [T][F_shared]
+ *   shared_hidden_scale [F_shared/128][T][4]  (MXFP8 only; else 0)
+ * Host-only; enqueues nothing.  Errors as glm_moe_workspace_size_ex. */
+typedef struct {
+  size_t row_assign, hidden, hidden_scale, shared_hidden, shared_hidden_scale;
+} glm_moe_hidden_layout;
+GLM_MOE_API int glm_moe_hidden_layout_of(const glm_moe_dims* d, const glm_moe_options* opts,
+                                         int top_k, glm_moe_hidden_layout* layout);
+
 /* Reorder MX scales from row-major [n_mats][N][K/32] (src) to the
  * K-step-major layout [n_mats][K/128][N][4] (dst) that glm_moe_forward_mx
  * reads; a pure byte permutation, run on `stream`.  Both are device

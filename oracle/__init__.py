@@ -5,11 +5,13 @@ and the CPU-baseline leg of ``bench.py``; never by the product package.
 """
 from . import mx
 from .moe import (Routing, bf16_bits_to_f64, block_ffn, decode, dense_ffn, expert_load,
-                  expert_mlp, expert_mlp_mx, forward, forward_arrays, forward_mx, group_scores,
+                  expert_hidden_mx, expert_mlp, expert_mlp_mx, forward, forward_arrays, forward_mx,
+                  forward_mx_on_hidden, group_scores,
                   rmsnorm, round_bf16, route, select_topk, select_topk_grouped, sigmoid, silu,
                   topk_gap)
 
 __all__ = ["Routing", "bf16_bits_to_f64", "block_ffn", "decode", "dense_ffn", "expert_load",
-           "expert_mlp", "expert_mlp_mx", "forward", "forward_arrays", "forward_mx",
+           "expert_hidden_mx", "expert_mlp", "expert_mlp_mx", "forward", "forward_arrays",
+           "forward_mx", "forward_mx_on_hidden",
            "group_scores", "mx", "rmsnorm", "round_bf16", "route", "select_topk",
            "select_topk_grouped", "sigmoid", "silu", "topk_gap"]

@@ -247,6 +247,13 @@ MxTensor = Tuple[np.ndarray, np.ndarray]        # (E4M3 codes, E8M0 scales)
 MxExpert = Tuple[MxTensor, MxTensor, MxTensor]  # w1, w3, w2
 
 
+def expert_hidden_mx(xq: np.ndarray, w1: MxTensor, w3: MxTensor) -> np.ndarray:
+    """The gated hidden values SiLU(x w1^T) * (x w3^T) of the MXFP8 expert MLP,
+    before they are quantised (``xq``: values of the quantised input rows)."""
+    W1, W3 = mx.dequantize(*w1), mx.dequantize(*w3)
+    return silu(xq @ W1.T) * (xq @ W3.T)
+
+
 def expert_mlp_mx(xq: np.ndarray, w1: MxTensor, w3: MxTensor, w2: MxTensor) -> np.ndarray:
     """The SiLU-gated expert MLP with MXFP8 weights, on an MXFP8 input.
 
@@ -255,9 +262,27 @@ def expert_mlp_mx(xq: np.ndarray, w1: MxTensor, w3: MxTensor, w2: MxTensor) -> n
     dimension before the w2 product, as the down projection consumes it in that
     format.
     """
-    W1, W3, W2 = mx.dequantize(*w1), mx.dequantize(*w3), mx.dequantize(*w2)
-    h = silu(xq @ W1.T) * (xq @ W3.T)
-    return mx.fake_quantize(h) @ W2.T
+    h = expert_hidden_mx(xq, w1, w3)
+    return mx.fake_quantize(h) @ mx.dequantize(*w2).T
+
+
+def forward_mx_on_hidden(routing: Routing, hidden: np.ndarray, shared_hidden: np.ndarray,
+                         experts: Callable[[int], MxExpert], shared: MxExpert) -> np.ndarray:
+    """Steps 5-6 of the MXFP8 layer from given quantised hidden values.
+
+    ``hidden[t, j]`` holds the values of token t's quantised gated hidden row
+    for slot j (expert ``routing.idx[t, j]``), ``shared_hidden[t]`` the shared
+    expert's.  Returns out[t] = sum_j w[t, j] (hidden[t, j] w2_e^T)
+    + shared_hidden[t] w2_shared^T.
+    """
+    T, k, _ = hidden.shape
+    D = mx.dequantize(*shared[2]).shape[0]
+    routed = np.zeros((T, D))
+    for e in np.unique(routing.idx):
+        tok, slot = np.nonzero(routing.idx == e)
+        y = hidden[tok, slot] @ mx.dequantize(*experts(int(e))[2]).T
+        routed[tok] += routing.weight[tok, slot][:, None] * y
+    return routed + shared_hidden @ mx.dequantize(*shared[2]).T
 
 
 def forward_mx(x, router_w, corr_bias,

@@ -150,6 +150,71 @@ WEIGHT_TOL = 1e-5
 MX_HW_REL = 2.0 ** -13
 
 
+def mx_hidden_budget(xq: np.ndarray, w1, w3, eps: float = MX_HW_REL):
+    """The oracle's gated hidden values h = SiLU(xq W1^T) * (xq W3^T) of an
+    MXFP8 expert (``oracle.expert_hidden_mx``) and the error budget ``eh`` of a
+    kernel's fp32 value of h: each product may be off by ``eps`` times the sum
+    of its term magnitudes, propagated to first order through SiLU(g) * u, plus
+    their product and a few fp32 roundings of the epilogue (2^-20 |h|)."""
+    W1, W3 = mx.dequantize(*w1), mx.dequantize(*w3)
+    h = moe.expert_hidden_mx(xq, w1, w3)
+    g, u = xq @ W1.T, xq @ W3.T
+    ax = np.abs(xq)
+    eg, eu = eps * (ax @ np.abs(W1).T), eps * (ax @ np.abs(W3).T)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    eh = (np.abs(sg * (1.0 + g * (1.0 - sg)) * u) * eg + np.abs(g * sg) * eu + eg * eu
+          + 2.0 ** -20 * np.abs(h))
+    return h, eh
+
+
+@dataclasses.dataclass
+class MxHiddenReport:
+    values: int          # hidden values checked
+    same: int            # kernel code and block scale equal to the oracle's rounding of h
+    other_valid: int     # different, but the rounding of a value within the budget of h
+    invalid: int         # neither
+    blocks: int
+    scale_other: int     # block scales different from the oracle's but valid
+    scale_invalid: int
+
+
+def mx_hidden_check(codes: np.ndarray, scales: np.ndarray, h: np.ndarray,
+                    eh: np.ndarray) -> MxHiddenReport:
+    """A kernel's MXFP8 hidden rows (E4M3 ``codes`` [n, F], E8M0 ``scales``
+    [n, F/32]) against the oracle's values ``h`` with error budget ``eh``.
+
+    The kernel takes each rounding decision once, on its own fp32 value of h.
+    A decision is valid when it is the oracle's rounding rule applied to some
+    value within ``eh`` of h:
+      * block scale 2^s: block_exponent(a) == s for some block maximum a in
+        [max(|h| - eh), max(|h| + eh)] (block_exponent is monotone);
+      * element code q (value at the kernel's scale): |q - h| <= eh + half the
+        E4M3 spacing at q's magnitude (the largest distance from which
+        round-to-nearest lands on q).
+    """
+    n, F = h.shape
+    nb = F // mx.BLOCK
+    s_k = np.asarray(scales).astype(np.int64).reshape(n, nb) - 127
+    q = mx.dequantize(codes, scales)
+    oc, osc = mx.quantize(h)
+    same = (np.asarray(codes) == oc) & np.repeat(np.asarray(scales).reshape(n, nb) == osc,
+                                                  mx.BLOCK, axis=1)
+    hb, eb = np.abs(h).reshape(n, nb, mx.BLOCK), eh.reshape(n, nb, mx.BLOCK)
+    lo = np.maximum(hb - eb, 0.0).max(axis=-1)
+    hi = (hb + eb).max(axis=-1)
+    s_lo = np.where(lo > 0, mx.block_exponent(lo), np.iinfo(np.int64).min)
+    s_hi = mx.block_exponent(hi)
+    scale_ok = (s_lo <= s_k) & (s_k <= s_hi)
+    sc = np.repeat(np.ldexp(1.0, s_k), mx.BLOCK, axis=1)
+    y = np.abs(q) / sc
+    _, x = np.frexp(np.maximum(y, 2.0 ** -6))
+    half = np.ldexp(1.0, x - 1 - 3) / 2 * sc       # half the spacing of y's binade, scaled
+    elem_ok = np.abs(q - h) <= eh + half
+    return MxHiddenReport(int(h.size), int(same.sum()), int((~same & elem_ok).sum()),
+                          int((~elem_ok).sum()), int(n * nb),
+                          int((scale_ok & (s_k + 127 != osc)).sum()), int((~scale_ok).sum()))
+
+
 def _e4m3_neighbours(a: np.ndarray):
     """The E4M3 grid values below and above |a| (a in [0, 448])."""
     _, x = np.frexp(np.maximum(a, 2.0 ** -6))

@@ -5,12 +5,12 @@ The layer runs in hand-written HIP kernels behind the C ABI of
 binding.  Build the library with ``python -m sparse_moe_transformer_glm_amd.build``.
 """
 from ._lib import (BF16, EHIP, EINVAL, EUNSUPPORTED, EWORKSPACE, F32, LIB_PATH, MXFP8, OK,
-                   STAGES, GlmMoeError, MxWeights, Options, Trace, dense_ffn, dense_workspace_size,
-                   forward, forward_mx, lib, new_workspace, options, pack_mx_scales, route,
+                   STAGES, GlmMoeError, HiddenLayout, MxWeights, Options, Trace, dense_ffn, dense_workspace_size,
+                   forward, forward_mx, hidden_layout, lib, new_workspace, options, pack_mx_scales, route,
                    workspace_bytes, workspace_size)
 
 __all__ = ["BF16", "EHIP", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "F32", "LIB_PATH", "MXFP8",
-           "OK", "STAGES", "GlmMoeError", "MxWeights", "Options", "Trace", "dense_ffn",
-           "dense_workspace_size", "forward", "forward_mx", "lib", "new_workspace", "options",
+           "OK", "STAGES", "GlmMoeError", "HiddenLayout", "MxWeights", "Options", "Trace", "dense_ffn",
+           "dense_workspace_size", "forward", "forward_mx", "hidden_layout", "lib", "new_workspace", "options",
            "pack_mx_scales",
            "route", "workspace_bytes", "workspace_size"]

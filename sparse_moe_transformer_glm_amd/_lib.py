@@ -41,6 +41,12 @@ class Options(ctypes.Structure):
                 ("norm_eps", ctypes.c_float), ("add_residual", ctypes.c_int32)]
 
 
+class HiddenLayout(ctypes.Structure):
+    """``glm_moe_hidden_layout``: workspace offsets of the gated hidden rows."""
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "row_assign", "hidden", "hidden_scale", "shared_hidden", "shared_hidden_scale")]
+
+
 class MxWeights(ctypes.Structure):
     """``glm_moe_mx_weights``: E4M3 code tensors and their E8M0 scales."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
@@ -64,6 +70,7 @@ def lib() -> ctypes.CDLL:
         pd, po = ctypes.POINTER(Dims), ctypes.POINTER(Options)
         L.glm_moe_workspace_size.argtypes = [pd, i32, ctypes.POINTER(sz)]
         L.glm_moe_workspace_size_ex.argtypes = [pd, po, i32, ctypes.POINTER(sz)]
+        L.glm_moe_hidden_layout_of.argtypes = [pd, po, i32, ctypes.POINTER(HiddenLayout)]
         L.glm_moe_workspace_bytes.argtypes = [pd, i32]
         L.glm_moe_workspace_bytes.restype = sz
         L.glm_moe_route.argtypes = [pd, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
@@ -91,7 +98,7 @@ def lib() -> ctypes.CDLL:
                      "glm_moe_route_ex", "glm_moe_forward", "glm_moe_forward_traced",
                      "glm_moe_forward_ex", "glm_moe_forward_mx", "glm_moe_dense_workspace_size", "glm_moe_dense_ffn",
                      "glm_moe_trace_create", "glm_moe_trace_destroy", "glm_moe_trace_reset",
-                     "glm_moe_trace_read", "glm_moe_mx_pack_scales"):
+                     "glm_moe_trace_read", "glm_moe_mx_pack_scales", "glm_moe_hidden_layout_of"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -149,6 +156,17 @@ def workspace_bytes(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
     if n == 0 and T > 0:
         raise GlmMoeError(EINVAL, "glm_moe_workspace_bytes", L.glm_moe_last_error().decode())
     return int(n)
+
+
+def hidden_layout(T: int, D: int, E: int, F: int, Fs: int, top_k: int,
+                  dtype: torch.dtype = torch.bfloat16, opts: Optional[Options] = None,
+                  weight: Optional[int] = None) -> HiddenLayout:
+    """Workspace offsets of the gated hidden rows (``glm_moe_hidden_layout_of``)."""
+    lay = HiddenLayout()
+    _check(lib().glm_moe_hidden_layout_of(ctypes.byref(dims(T, D, E, F, Fs, dtype, weight)),
+                                          None if opts is None else ctypes.byref(opts), top_k,
+                                          ctypes.byref(lay)), "glm_moe_hidden_layout_of")
+    return lay
 
 
 def dense_workspace_size(T: int, D: int, F: int, dtype: torch.dtype = torch.bfloat16,

@@ -447,6 +447,20 @@ int glm_moe_workspace_size(const glm_moe_dims* d, int top_k, size_t* bytes) {
   return glm_moe_workspace_size_ex(d, nullptr, top_k, bytes);
 }
 
+int glm_moe_hidden_layout_of(const glm_moe_dims* d, const glm_moe_options* opts, int top_k,
+                             glm_moe_hidden_layout* layout) {
+  if (!layout) return fail(GLM_MOE_EINVAL, "layout is null");
+  Plan P;
+  int st = make_plan(d, top_k, opts, false, &P);
+  if (st) return st;
+  layout->row_assign = P.row_assign;
+  layout->hidden = P.H;
+  layout->hidden_scale = P.mx ? P.Hsc : 0;
+  layout->shared_hidden = P.Hs;
+  layout->shared_hidden_scale = P.mx ? P.Hssc : 0;
+  return GLM_MOE_OK;
+}
+
 size_t glm_moe_workspace_bytes(const glm_moe_dims* d, int top_k) {
   g_err[0] = 0;
   size_t n = 0;

@@ -248,3 +248,53 @@ def test_mx_explain_flags_small_output_errors():
     rms = np.sqrt((ref ** 2).mean())
     bad[3, 7] += 1e-2 * rms
     assert parity.mx_explain(bad, ref, x, r, lambda e: ex[e], sh).violations == 1
+
+
+# --------------------------------------------- MXFP8 hidden-value decisions
+
+def _mx_hidden(seed=3, n=6, F=128):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((n, F)) * np.exp(rng.normal(0, 1, (n, 1)))
+    codes, scales = oracle.mx.quantize(h)
+    return h, codes, scales
+
+
+def test_mx_hidden_check_accepts_the_oracle_rounding():
+    h, codes, scales = _mx_hidden()
+    rep = parity.mx_hidden_check(codes, scales, h, 1e-9 * np.abs(h))
+    assert rep.same == rep.values == h.size
+    assert rep.invalid == rep.other_valid == rep.scale_invalid == rep.scale_other == 0
+
+
+def test_mx_hidden_check_takes_a_flip_at_a_midpoint_only_within_budget():
+    h, codes, scales = _mx_hidden()
+    mx = oracle.mx
+    # move element (2, 5) onto the midpoint between its code and the next one up
+    s = np.ldexp(1.0, scales[2, 0].astype(np.int64) - 127)
+    y = abs(h[2, 5]) / s
+    lo_code = mx.encode_e4m3(np.array([y]))[0]
+    v0 = mx.decode_e4m3(np.array([lo_code]))[0]
+    nxt = mx.decode_e4m3(np.array([lo_code + 1]))[0]
+    h[2, 5] = np.sign(h[2, 5]) * (v0 + nxt) / 2 * s * (1 - 1e-9)  # just below the midpoint
+    codes, scales = mx.quantize(h)
+    flipped = codes.copy()
+    flipped[2, 5] = codes[2, 5] + 1 if mx.decode_e4m3(codes[2, 5:6])[0] == np.sign(h[2, 5]) * v0 \
+        else codes[2, 5] - 1
+    eh = 1e-6 * np.abs(h)
+    rep = parity.mx_hidden_check(flipped, scales, h, eh)
+    assert (rep.same, rep.other_valid, rep.invalid) == (h.size - 1, 1, 0)
+    # the same flip two codes away is not a rounding of any value in budget
+    far = codes.copy()
+    far[2, 5] = flipped[2, 5] + (flipped[2, 5].astype(int) - codes[2, 5].astype(int))
+    assert parity.mx_hidden_check(far, scales, h, eh).invalid == 1
+
+
+def test_mx_hidden_check_rejects_a_wrong_scale_and_a_permuted_row():
+    h, codes, scales = _mx_hidden()
+    bad = scales.copy()
+    bad[1, 2] += 1   # one binade too coarse: within range, but not the rule's choice
+    rep = parity.mx_hidden_check(codes, bad, h, 1e-9 * np.abs(h))
+    assert rep.scale_invalid == 1 and rep.invalid > 0
+    # rows swapped (an indexing mistake): almost every value is invalid
+    rep = parity.mx_hidden_check(codes[::-1].copy(), scales[::-1].copy(), h, 1e-6 * np.abs(h))
+    assert rep.invalid > 0.8 * h.size
