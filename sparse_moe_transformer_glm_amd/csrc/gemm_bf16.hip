@@ -77,6 +77,166 @@ struct Cfg {
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Global address (K offset 0) of row r of a tile's operand rows: r < BM is
+// an A row (rows past the tile's valid rows repeat its last valid row), else
+// B row r - BM.  Gate/up B rows alternate MB rows of w1 (gate) with the
+// matching MB rows of w3 (up).
+template <int MODE, int BM, int MB>
+__device__ __forceinline__ const bf16_t* tile_row_src(const GateUpArgs& gu, const DownArgs& dn,
+                                                      int g, int row0, int rows, int col0, int r) {
+  if (r < BM) {
+    const int rr = min(r, rows - 1);
+    if constexpr (MODE == GATE_UP) {
+      const int tok = (g == gu.E) ? row0 + rr : gu.row_assign[row0 + rr] / gu.k;
+      return gu.x + (size_t)tok * gu.D;
+    } else {
+      return (g == dn.E) ? dn.Hs + (size_t)(row0 + rr) * dn.Fs
+                         : dn.H + (size_t)(row0 + rr) * dn.F;
+    }
+  }
+  const int n = r - BM;
+  if constexpr (MODE == GATE_UP) {
+    const int blk = n / MB, hcol = col0 + (blk / 2) * MB + (n % MB);
+    const bool up = blk & 1;
+    if (g == gu.E) return (up ? gu.sw3 : gu.sw1) + (size_t)hcol * gu.D;
+    return (up ? gu.w3 : gu.w1) + ((size_t)g * gu.F + hcol) * gu.D;
+  } else {
+    return (g == dn.E) ? dn.sw2 + (size_t)(col0 + n) * dn.Fs
+                       : dn.w2 + ((size_t)g * dn.D + col0 + n) * dn.F;
+  }
+}
+
+// Epilogue of a tile: every wave writes its (TM x TN) accumulators.
+//  * GATE_UP: H = bf16(SiLU(g) * u) of its hidden columns; with `hblk` (a
+//    per-wave LDS scratch of MB x TN/2 bf16, used when GU_LDS) one MB-row block
+//    at a time through LDS with 16-byte stores, else straight from the
+//    accumulators.
+//  * DOWN: Y[t][j] = w * acc to the row's (token, slot) place; `s_asg` /
+//    `s_wt` (BM entries each) take every row's Y row and weight; with `yblk`
+//    (a per-wave LDS scratch of MB x TN fp32, used when DN_LDS) through LDS
+//    with 16-byte stores.
+// The LDS regions may alias the operand stages: the function starts with a
+// workgroup barrier after which no wave reads them any more.
+template <class C, int MODE, bool GU_LDS, bool DN_LDS, class Acc>
+__device__ __forceinline__ void tile_epilogue(const GateUpArgs& gu, const DownArgs& dn,
+                                              Acc (&acc)[C::FM][C::FN], int g, int row0, int rows,
+                                              int col0, int wrow0, int live_m, int row_a,
+                                              float row_wt, bf16_t* hblk, float* yblk, int* s_asg,
+                                              float* s_wt) {
+  constexpr int MB = C::MB, FM = C::FM, FN = C::FN, TN = C::TN, WN = C::WN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wn = wave % WN;
+  const int lr = lane % MB, lk = lane / MB;
+  // accumulator element r of block (m, n):
+  //   MB = 32: row 8*(r/4) + 4*(lane/32) + r%4, column lane % 32
+  //   MB = 16: row 4*(lane/16) + r,             column lane % 16
+  constexpr int NR = MB == 32 ? 16 : 4;
+  auto row_of = [&](int m, int r) {
+    return wrow0 + m * MB + (MB == 32 ? 8 * (r / 4) + 4 * lk + (r % 4) : 4 * lk + r);
+  };
+  if constexpr (MODE == GATE_UP) {
+    const bool shared = (g == gu.E);
+    const int F = shared ? gu.Fs : gu.F;
+    bf16_t* Hb = (shared ? gu.Hs : gu.H) + (size_t)row0 * F;
+    constexpr int HC = TN / 2;  // hidden columns of this wave
+    __syncthreads();            // every wave is done reading the stages
+    if constexpr (GU_LDS) {
+      // Through LDS, one MB-row block at a time (as the down epilogue):
+      // 16-byte stores of 8 consecutive hidden values.
+      constexpr int CG = HC / 8 > 0 ? HC / 8 : 1, RPP = kWave / CG;
+      static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
+      const int hcol0 = col0 + wn * HC;
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const int rb = row_of(m, r) - (wrow0 + m * MB);
+            const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
+            hblk[rb * HC + q * MB + lr] = f32_to_bf16(h);
+          }
+#pragma unroll
+        for (int pass = 0; pass < MB / RPP; ++pass) {
+          const int rb = pass * RPP + lane / CG, cg = lane % CG;
+          const int row = wrow0 + m * MB + rb;
+          const uint4 v = *reinterpret_cast<const uint4*>(hblk + rb * HC + 8 * cg);
+          if (row < rows) *reinterpret_cast<uint4*>(Hb + (size_t)row * F + hcol0 + 8 * cg) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q) {
+          const int hcol = col0 + (wn * TN / (2 * MB) + q) * MB + lr;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const int row = row_of(m, r);
+            if (row < rows) {
+              const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
+              Hb[(size_t)row * F + hcol] = f32_to_bf16(h);
+            }
+          }
+        }
+      }
+    }
+  } else {
+    __syncthreads();  // every wave is done reading the stages (s_asg may alias one)
+    // row of Y and routing weight of every row of the tile
+    if (tid < rows) {
+      s_asg[tid] = g == dn.E ? (row0 + tid) * (dn.k + 1) + dn.k : y_row(row_a, dn.k);
+      s_wt[tid] = row_wt;
+    }
+    __syncthreads();  // the row table is complete
+    if constexpr (DN_LDS) {
+      // Through LDS, one MB-row block at a time: each wave writes its block
+      // (MB x TN fp32) to its own scratch, then stores whole 16-byte column
+      // groups, so a store instruction covers a few full row pieces.
+      constexpr int CG = TN / 4;            // 16-byte column groups per row
+      constexpr int RPP = kWave / CG;       // rows per pass
+      static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int rb = row_of(m, r) - (wrow0 + m * MB);
+#pragma unroll
+          for (int n = 0; n < FN; ++n) yblk[rb * TN + n * MB + lr] = acc[m][n][r];
+        }
+#pragma unroll
+        for (int pass = 0; pass < MB / RPP; ++pass) {
+          const int rb = pass * RPP + lane / CG, cg = lane % CG;
+          const int row = wrow0 + m * MB + rb;
+          const float4 v = *reinterpret_cast<const float4*>(yblk + rb * TN + 4 * cg);
+          if (row < rows) {
+            const float w = s_wt[row];
+            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
+            store_stream(y, f32x4{w * v.x, w * v.y, w * v.z, w * v.w});
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int row = row_of(m, r);
+          if (row < rows) {
+            const float w = s_wt[row];
+            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
+#pragma unroll
+            for (int n = 0; n < FN; ++n) store_stream(y + n * MB, w * acc[m][n][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
 
 
 // EARLY (two stages only): each stage's refill is issued before the wait for
@@ -129,30 +289,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     const int q = wave + i * NW;
     const int r = q * RPI + lane / CPR;
     const int ch = (lane % CPR) ^ swz<BK>(r);
-    const bf16_t* base;
-    if (r < BM) {
-      const int rr = min(r, rows - 1);  // rows past the tile repeat its last row
-      if constexpr (MODE == GATE_UP) {
-        const int tok = (g == gu.E) ? row0 + rr
-                                    : gu.row_assign[row0 + rr] / gu.k;
-        base = gu.x + (size_t)tok * gu.D;
-      } else {
-        base = (g == dn.E) ? dn.Hs + (size_t)(row0 + rr) * dn.Fs
-                           : dn.H + (size_t)(row0 + rr) * dn.F;
-      }
-    } else {
-      const int n = r - BM;
-      if constexpr (MODE == GATE_UP) {
-        const int blk = n / MB, hcol = col0 + (blk / 2) * MB + (n % MB);
-        const bool up = blk & 1;
-        if (g == gu.E) base = (up ? gu.sw3 : gu.sw1) + (size_t)hcol * gu.D;
-        else base = (up ? gu.w3 : gu.w1) + ((size_t)g * gu.F + hcol) * gu.D;
-      } else {
-        base = (g == dn.E) ? dn.sw2 + (size_t)(col0 + n) * dn.Fs
-                           : dn.w2 + ((size_t)g * dn.D + col0 + n) * dn.F;
-      }
-    }
-    src[i] = base + ch * 8;
+    src[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + ch * 8;
   }
 
   // Per-row data of the down epilogue (assignment and routing weight of row
@@ -339,117 +476,229 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   }
 
   // ------------------------------------------------------------ epilogue
-  // accumulator element r of block (m, n):
-  //   MB = 32: row 8*(r/4) + 4*(lane/32) + r%4, column lane % 32
-  //   MB = 16: row 4*(lane/16) + r,             column lane % 16
-  constexpr int NR = MB == 32 ? 16 : 4;
-  auto row_of = [&](int m, int r) {
-    return wrow0 + m * MB + (MB == 32 ? 8 * (r / 4) + 4 * lk + (r % 4) : 4 * lk + r);
-  };
+  // (through LDS where stage 0 is large enough for every wave's block)
+  constexpr int HC = TN / 2;
+  constexpr bool GU_LDS = NW * MB * HC * 2 <= C::STAGE * 2 && HC % 8 == 0 &&
+                          MB % (kWave / (HC / 8 > 0 ? HC / 8 : 1)) == 0;
+  constexpr bool DN_LDS = NW * MB * TN * 4 <= C::STAGE * 2;
+  tile_epilogue<C, MODE, GU_LDS, DN_LDS>(gu, dn, acc, g, row0, rows, col0, wrow0, live_m, row_a, row_wt,
+                         GU_LDS ? lds0 + wave * (MB * HC) : nullptr,
+                         DN_LDS ? reinterpret_cast<float*>(lds0) + wave * (MB * TN) : nullptr,
+                         s_asg, s_wt);
+}
+
+// Split rings for the 256 x 256 prefill tiles.  The A rows (token
+// activations or hidden rows: each is re-read by every column tile of its
+// group, so mostly L2 hits) and the B rows (weights: streamed from HBM by the
+// first tile that needs them) go through separate rings of 32 KB slots: two
+// A slots and three B slots (the whole 160 KB of LDS).  At the end of step kt
+// a wave waits for step kt+1, meets the workgroup barrier and refills the
+// slots step kt used with the A rows of step kt+2 and the B rows of step
+// kt+3, so the weight rows run two K steps ahead of the math with one
+// barrier per step.  Each slot is its own LDS object, so the compiler tracks
+// the LDS-DMA copies per slot.  Rows are 128-byte pieces (K step 64): a
+// narrower step would issue two requests per cache line.
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownArgs dn) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MB = C::MB;
+  constexpr int WN = C::WN, NW = C::NW, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+  constexpr int CPR = C::CPR, RPI = C::RPI;
+  constexpr int AW = C::A_INST / NW, BW = C::B_INST / NW;  // copies per wave and step
+  static_assert(C::A_INST % NW == 0 && C::B_INST % NW == 0, "whole copies per wave");
+  static_assert(C::KSUB % 2 == 0 && FM <= 4, "fragment slots and live-block dispatch");
+  constexpr int HC = TN / 2;
+  static_assert(NW * MB * HC <= BM * BK && (NW / 2) * MB * TN * 2 <= BN * BK &&
+                    2 * BM * 4 <= BM * BK * 2,
+                "epilogue scratch fits the ring slots");
+
+  __shared__ __attribute__((aligned(1024))) bf16_t la0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t la1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t lb0[BN * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t lb1[BN * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t lb2[BN * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0;
   if constexpr (MODE == GATE_UP) {
-    const bool shared = (g == gu.E);
-    const int F = shared ? gu.Fs : gu.F;
-    bf16_t* Hb = (shared ? gu.Hs : gu.H) + (size_t)row0 * F;
-    constexpr int HC = TN / 2;  // hidden columns of this wave
-    if constexpr (NW * MB * HC * 2 <= C::STAGE * 2 && HC % 8 == 0 &&
-                  MB % (kWave / (HC / 8 > 0 ? HC / 8 : 1)) == 0) {
-      // Through LDS, one MB-row block at a time (as the down epilogue):
-      // 16-byte stores of 8 consecutive hidden values.
-      bf16_t* blk = lds0 + wave * (MB * HC);
-      constexpr int CG = HC / 8, RPP = kWave / CG;
-      static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
-      const int hcol0 = col0 + wn * HC;
-      __syncthreads();  // every wave is done reading the stages
-#pragma unroll
-      for (int m = 0; m < FM; ++m) {
-        if (m >= live_m) continue;
-#pragma unroll
-        for (int q = 0; q < FN / 2; ++q)
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const int rb = row_of(m, r) - (wrow0 + m * MB);
-            const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
-            blk[rb * HC + q * MB + lr] = f32_to_bf16(h);
-          }
-#pragma unroll
-        for (int pass = 0; pass < MB / RPP; ++pass) {
-          const int rb = pass * RPP + lane / CG, cg = lane % CG;
-          const int row = wrow0 + m * MB + rb;
-          const uint4 v = *reinterpret_cast<const uint4*>(blk + rb * HC + 8 * cg);
-          if (row < rows) *reinterpret_cast<uint4*>(Hb + (size_t)row * F + hcol0 + 8 * cg) = v;
-        }
-      }
-    } else {
-#pragma unroll
-    for (int m = 0; m < FM; ++m) {
-      if (m >= live_m) continue;
-#pragma unroll
-      for (int q = 0; q < FN / 2; ++q) {
-        const int hcol = col0 + (wn * TN / (2 * MB) + q) * MB + lr;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int row = row_of(m, r);
-          if (row < rows) {
-            const float h = silu(acc[m][2 * q][r]) * acc[m][2 * q + 1][r];
-            Hb[(size_t)row * F + hcol] = f32_to_bf16(h);
-          }
-        }
-      }
-    }
-    }
+    const int i = xcd_tile(*gu.desc_count, gu.xblk);
+    if (i < 0) return;
+    const TileDesc d = gu.desc[i];
+    g = d.group & kGroupMask; row0 = d.row0; rows = d.rows; col0 = d.col0; K = gu.D;
   } else {
-    // row of Y and routing weight of every row of the tile
-    if (tid < rows) {
-      s_asg[tid] = g == dn.E ? (row0 + tid) * (dn.k + 1) + dn.k : y_row(row_a, dn.k);
-      s_wt[tid] = row_wt;
-    }
-    __syncthreads();  // the row table is complete and every wave is done reading the stages
-    if constexpr (NW * MB * TN * 4 <= C::STAGE * 2) {
-      // Through LDS, one MB-row block at a time: each wave writes its block
-      // (MB x TN fp32) to its own slice of stage 0, then stores whole 16-byte
-      // column groups, so a store instruction covers a few full row pieces.
-      float* blk = reinterpret_cast<float*>(lds0) + wave * (MB * TN);
-      constexpr int CG = TN / 4;            // 16-byte column groups per row
-      constexpr int RPP = kWave / CG;       // rows per pass
-      static_assert(kWave % CG == 0 && MB % RPP == 0, "epilogue pass shape");
+    const int i = xcd_tile(*dn.desc_count, dn.xblk);
+    if (i < 0) return;
+    const TileDesc d = dn.desc[i];
+    g = d.group & kGroupMask; row0 = d.row0; rows = d.rows; col0 = d.col0;
+    K = (g == dn.E) ? dn.Fs : dn.F;
+  }
+
+  // copy i of a wave covers operand rows (wave + i*NW)*RPI .. +RPI of a slot;
+  // lane l fills physical chunk l % CPR of its row, logical chunk (l % CPR) ^ swz
+  const bf16_t* sa[AW];
+  const bf16_t* sb[BW];
 #pragma unroll
-      for (int m = 0; m < FM; ++m) {
-        if (m >= live_m) continue;
+  for (int i = 0; i < AW; ++i) {
+    const int r = (wave + i * NW) * RPI + lane / CPR;
+    sa[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) +
+            ((lane % CPR) ^ swz<BK>(r)) * 8;
+  }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int rb = row_of(m, r) - (wrow0 + m * MB);
-#pragma unroll
-          for (int n = 0; n < FN; ++n) blk[rb * TN + n * MB + lr] = acc[m][n][r];
-        }
-#pragma unroll
-        for (int pass = 0; pass < MB / RPP; ++pass) {
-          const int rb = pass * RPP + lane / CG, cg = lane % CG;
-          const int row = wrow0 + m * MB + rb;
-          const float4 v = *reinterpret_cast<const float4*>(blk + rb * TN + 4 * cg);
-          if (row < rows) {
-            const float w = s_wt[row];
-            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + 4 * cg;
-            store_stream(y, f32x4{w * v.x, w * v.y, w * v.z, w * v.w});
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < FM; ++m) {
-        if (m >= live_m) continue;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int row = row_of(m, r);
-          if (row < rows) {
-            const float w = s_wt[row];
-            float* y = dn.Y + (size_t)s_asg[row] * dn.D + col0 + wn * TN + lr;
-#pragma unroll
-            for (int n = 0; n < FN; ++n) store_stream(y + n * MB, w * acc[m][n][r]);
-          }
-        }
-      }
+  for (int i = 0; i < BW; ++i) {
+    const int n = (wave + i * NW) * RPI + lane / CPR;
+    sb[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, BM + n) +
+            ((lane % CPR) ^ swz<BK>(n)) * 8;
+  }
+
+  static_assert(BM <= C::NT, "one epilogue row per thread");
+  int row_a = 0;
+  float row_wt = 1.0f;
+  if constexpr (MODE == DOWN) {
+    if (tid < rows && g != dn.E) {
+      row_a = dn.row_assign[row0 + tid];
+      row_wt = dn.row_w[row0 + tid];
     }
   }
+
+  auto a_slot = [&](int s) -> bf16_t* { return s == 0 ? la0 : la1; };
+  auto b_slot = [&](int s) -> bf16_t* { return s == 0 ? lb0 : s == 1 ? lb1 : lb2; };
+  auto issueA = [&](bf16_t* st, int kt) {
+#pragma unroll
+    for (int i = 0; i < AW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(sa[i] + (size_t)kt * BK),
+                                       (lds_void*)(st + (wave + i * NW) * (RPI * BK)), 16, 0, 0);
+  };
+  auto issueB = [&](bf16_t* st, int kt) {
+#pragma unroll
+    for (int i = 0; i < BW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(sb[i] + (size_t)kt * BK),
+                                       (lds_void*)(st + (wave + i * NW) * (RPI * BK)), 16, 0, 0);
+  };
+
+  const int nk = K / BK;
+  // A rows of steps 0 and 1 and B rows of steps 0..2, in step order; wait
+  // for step 0
+  auto prologue = [&]() {
+    issueA(la0, 0);
+    issueB(lb0, 0);
+    if (nk > 1) {
+      issueA(la1, 1);
+      issueB(lb1, 1);
+    }
+    if (nk > 2) {
+      issueB(lb2, 2);
+      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(AW + 2 * BW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+    }
+    lds_barrier();
+  };
+  // End of step kt: the copies issued after step kt+1's are at most the B
+  // rows of step kt+2; wait for step kt+1, barrier, refill step kt's slots.
+  // STEADY: steps kt+1 .. kt+3 exist (known at compile time).
+  auto handover = [&](auto sc, int kt, auto steady_c) {
+    constexpr int u = decltype(sc)::value;  // kt % 6
+    constexpr bool STEADY = decltype(steady_c)::value;
+    if (STEADY || kt + 2 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(BW));
+    else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
+    lds_barrier();
+    if (STEADY || kt + 2 < nk) issueA(a_slot(u % 2), kt + 2);
+    if (STEADY || kt + 3 < nk) issueB(b_slot(u % 3), kt + 3);
+  };
+
+  const int per = min(TM, ((rows + C::WM - 1) / C::WM + MB - 1) / MB * MB);
+  const int wrow0 = wm * per;
+  const int live_m = min(min(FM, per / MB), max(0, (rows - wrow0 + MB - 1) / MB));
+  const int lr = lane % MB, lk = lane / MB;
+  const int sw = swz<BK>(lr);
+
+  typedef f32x16 acc_t;
+  static_assert(MB == 32, "32 x 32 MFMA blocks");
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int m = 0; m < FM; ++m)
+#pragma unroll
+    for (int n = 0; n < FN; ++n) acc[m][n] = acc_t{};
+
+  auto run = [&](auto live_c) {
+    constexpr int LIVE = decltype(live_c)::value;
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto load_frags = [&](const bf16_t* sa_, const bf16_t* sb_, int sub, int slot) {
+      const int off = ((2 * sub + lk) ^ sw) * 8;
+      const bf16_t* pa = sa_ + (wrow0 + lr) * BK + off;
+      const bf16_t* pb = sb_ + (wn * TN + lr) * BK + off;
+#pragma unroll
+      for (int n = 0; n < FN; ++n)
+        fb[slot][n] = *reinterpret_cast<const bf16x8*>(pb + n * MB * BK);
+#pragma unroll
+      for (int m = 0; m < LIVE; ++m)
+        fa[slot][m] = *reinterpret_cast<const bf16x8*>(pa + m * MB * BK);
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+      for (int m = 0; m < LIVE; ++m)
+#pragma unroll
+        for (int n = 0; n < FN; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][m], fb[slot][n],
+                                                              acc[m][n], 0, 0, 0);
+    };
+    prologue();
+    load_frags(la0, lb0, 0, 0);
+    // one K step on the slots of step kt (u = kt % 6); the hand-over sits
+    // before the last sub-step's MFMAs, which cover the next slots' first reads
+    auto step = [&](auto sc, int kt, auto steady_c) {
+      constexpr int u = decltype(sc)::value;
+      constexpr bool STEADY = decltype(steady_c)::value;
+      const bf16_t* ca = a_slot(u % 2);
+      const bf16_t* cb = b_slot(u % 3);
+#pragma unroll
+      for (int sub = 0; sub < C::KSUB; ++sub) {
+        if (sub + 1 < C::KSUB) load_frags(ca, cb, sub + 1, (sub + 1) & 1);
+        if (sub == C::KSUB - 1 && (STEADY || kt + 1 < nk)) {
+          handover(sc, kt, steady_c);
+          load_frags(a_slot((u + 1) % 2), b_slot((u + 1) % 3), 0, 0);
+        }
+        // keep the reads issued above ahead of this sub-step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        mma(sub & 1);
+      }
+    };
+    int kt = 0;
+    for (; kt + 8 < nk; kt += 6)  // every step of the group has three steps after it
+      unroll<6>([&](auto uc) { step(uc, kt + decltype(uc)::value, std::true_type{}); });
+    for (; kt < nk; kt += 6)
+      unroll<6>([&](auto uc) {
+        if (kt + decltype(uc)::value < nk) step(uc, kt + decltype(uc)::value, std::false_type{});
+      });
+  };
+  switch (live_m) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    default: {
+      // this wave row holds no valid row: make its copies and keep the
+      // barrier count of the others
+      prologue();
+      int kt = 0;
+      for (; kt + 6 < nk; kt += 6)
+        unroll<6>([&](auto uc) { handover(uc, kt + decltype(uc)::value, std::false_type{}); });
+      for (; kt + 1 < nk; kt += 6)
+        unroll<6>([&](auto uc) {
+          if (kt + decltype(uc)::value + 1 < nk)
+            handover(uc, kt + decltype(uc)::value, std::false_type{});
+        });
+    }
+  }
+
+  // epilogue scratch in the ring slots (no copy is in flight any more):
+  // hidden blocks in la0, the row table in la1, fp32 blocks in lb0 / lb1
+  tile_epilogue<C, MODE, true, true>(
+      gu, dn, acc, g, row0, rows, col0, wrow0, live_m, row_a, row_wt, la0 + wave * (MB * HC),
+      reinterpret_cast<float*>(wave < NW / 2 ? lb0 : lb1) + (wave % (NW / 2)) * (MB * TN),
+      reinterpret_cast<int*>(la1), reinterpret_cast<float*>(la1) + BM);
 }
 
 // out[t][d] = Y[t][k][d] + Y[t][0][d] + ... + Y[t][k-1][d] (+ residual[t][d]),
@@ -510,9 +759,16 @@ using CfgMid = Cfg<GLM_CFG_MID>;
 using CfgBig = Cfg<GLM_CFG_BIG>;  // prefill: 8 waves (two per SIMD), BK 64, 2 stages
 using CfgNarrow = Cfg<32, 64, 64, 1, 2, 4, 16>;    // widths that are not a multiple of 128/256
 
+#ifndef GLM_SPLIT_BIG
+#define GLM_SPLIT_BIG 1
+#endif
 template <class C, int MODE>
 hipError_t launch_one(const GateUpArgs& gu, const DownArgs& dn, unsigned grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
+  if constexpr (C::BM == 256 && C::BN == 256 && C::BK == 64 && C::MB == 32 && GLM_SPLIT_BIG) {
+    split_gemm_kernel<C, MODE><<<grid, C::NT, 0, s>>>(gu, dn);
+    return hipGetLastError();
+  }
   if constexpr (C::ST == 2) {
     if (MODE == GATE_UP ? gu.early : dn.early) {
       grouped_gemm_kernel<C, MODE, true><<<grid, C::NT, 0, s>>>(gu, dn);

@@ -103,6 +103,16 @@ SMALL = {
     # element compared
     "early_rows": W(name="early_rows", T=640, D=256, E=8, k=2, F=256, Fs=256, seed=21,
                     weight_seed=21),
+    # >160 rows per expert on 256-row tiles (split rings): gate/up K = 512 and
+    # down K = 384 (8 and 6 K steps: every position of the six-step ring
+    # period, prologue and tail); an odd gate/up K step count (7) with D = 448
+    "big_even": W(name="big_even", T=3000, D=512, E=16, k=2, F=384, Fs=384, seed=23,
+                  weight_seed=23),
+    "big_odd": W(name="big_odd", T=2600, D=448, E=16, k=2, F=256, Fs=256, seed=24,
+                 weight_seed=24),
+    # 768-wide K (12 steps): the steady six-step loop runs once before the tail
+    "big_k768": W(name="big_k768", T=2400, D=768, E=12, k=2, F=256, Fs=256, seed=25,
+                  weight_seed=25),
     "f32_ragged": W("tiny_f32", name="f32_ragged", T=37, D=100, E=5, k=2, F=30, Fs=7, seed=19,
                     weight_seed=19),
     "f32_many": W("tiny_f32", name="f32_many", T=300, D=64, E=16, k=4, F=32, Fs=48, seed=20,
