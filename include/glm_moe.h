@@ -128,6 +128,27 @@ GLM_MOE_API int glm_moe_forward(const glm_moe_dims* d, const void* x, const floa
                     int32_t* topk_idx_out, float* topk_w_out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* glm_moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as glm_moe_forward without the workspace: the
+ * call works in a fixed 64 MiB buffer that the library holds on each GPU it
+ * runs on until the process ends (its address is looked up once per device,
+ * with that device current).  The call itself allocates and frees nothing.
+ * Sizes whose workspace (glm_moe_workspace_bytes) exceeds 64 MiB are rejected
+ * with GLM_MOE_EWORKSPACE before anything is enqueued; at the GLM-5.2 shape
+ * (hidden 6144, 256 experts, top-8, width 2048) that admits batches of up to
+ * 235 tokens, e.g. decode steps.  Every call on one GPU uses that GPU's
+ * buffer: calls that overlap on one GPU (on different streams or host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  Options (groups, norm, residual) and traces are not available here. */
+GLM_MOE_API int glm_moe_forward_noalloc(const glm_moe_dims* d, const void* x,
+                                        const float* router_w, const float* corr_bias,
+                                        const void* w1, const void* w3, const void* w2,
+                                        const void* shared_w1, const void* shared_w3,
+                                        const void* shared_w2, int top_k, float scale, float* out,
+                                        int32_t* topk_idx_out, float* topk_w_out,
+                                        hipStream_t stream);
+
 /* Stages of one forward call, in launch order (used by the stage trace). */
 enum {
   GLM_MOE_STAGE_NORM = 0,          /* pre-norm RMSNorm (empty unless requested) */

@@ -6,11 +6,11 @@ binding.  Build the library with ``python -m sparse_moe_transformer_glm_amd.buil
 """
 from ._lib import (BF16, EHIP, EINVAL, EUNSUPPORTED, EWORKSPACE, F32, LIB_PATH, MXFP8, OK,
                    STAGES, GlmMoeError, HiddenLayout, MxWeights, Options, Trace, dense_ffn, dense_workspace_size,
-                   forward, forward_mx, hidden_layout, lib, new_workspace, options, pack_mx_scales, route,
+                   forward, forward_mx, forward_noalloc, hidden_layout, lib, new_workspace, options, pack_mx_scales, route,
                    workspace_bytes, workspace_size)
 
 __all__ = ["BF16", "EHIP", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "F32", "LIB_PATH", "MXFP8",
            "OK", "STAGES", "GlmMoeError", "HiddenLayout", "MxWeights", "Options", "Trace", "dense_ffn",
-           "dense_workspace_size", "forward", "forward_mx", "hidden_layout", "lib", "new_workspace", "options",
+           "dense_workspace_size", "forward", "forward_mx", "forward_noalloc", "hidden_layout", "lib", "new_workspace", "options",
            "pack_mx_scales",
            "route", "workspace_bytes", "workspace_size"]

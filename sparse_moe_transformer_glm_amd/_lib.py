@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.glm_moe_forward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
                                       vp, sz, vp]
         L.glm_moe_forward_traced.argtypes = L.glm_moe_forward.argtypes + [vp]
+        L.glm_moe_forward_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32,
+                                              vp, vp, vp, vp]
         L.glm_moe_forward_ex.argtypes = [pd, po, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
                                          vp, vp, vp, sz, vp, vp]
         L.glm_moe_forward_mx.argtypes = [pd, po, vp, vp, vp, ctypes.POINTER(MxWeights), i32, f32,
@@ -98,7 +100,8 @@ def lib() -> ctypes.CDLL:
                      "glm_moe_route_ex", "glm_moe_forward", "glm_moe_forward_traced",
                      "glm_moe_forward_ex", "glm_moe_forward_mx", "glm_moe_dense_workspace_size", "glm_moe_dense_ffn",
                      "glm_moe_trace_create", "glm_moe_trace_destroy", "glm_moe_trace_reset",
-                     "glm_moe_trace_read", "glm_moe_mx_pack_scales", "glm_moe_hidden_layout_of"):
+                     "glm_moe_trace_read", "glm_moe_mx_pack_scales", "glm_moe_hidden_layout_of",
+                     "glm_moe_forward_noalloc"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -299,6 +302,33 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(),
         None if trace is None else trace.handle)
     _check(st, "glm_moe_forward_ex")
+    return out
+
+
+def forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, corr_bias: torch.Tensor,
+                    w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+                    shared_w1: torch.Tensor, shared_w3: torch.Tensor, shared_w2: torch.Tensor,
+                    top_k: int, scale: float, out: torch.Tensor,
+                    topk_idx: Optional[torch.Tensor] = None,
+                    topk_w: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``glm_moe_forward_noalloc``: the layer in the library's fixed per-GPU
+    workspace (no allocation; ``out`` must be given)."""
+    T, D = x.shape
+    E, F, _ = w1.shape
+    Fs = shared_w1.shape[0]
+    dt = x.dtype
+    st = lib().glm_moe_forward_noalloc(
+        ctypes.byref(dims(T, D, E, F, Fs, dt)), _ptr(x, "x", dt, (T, D)),
+        _ptr(router_w, "router_w", torch.float32, (E, D)),
+        _ptr(corr_bias, "corr_bias", torch.float32, (E,)),
+        _ptr(w1, "w1", dt, (E, F, D)), _ptr(w3, "w3", dt, (E, F, D)),
+        _ptr(w2, "w2", dt, (E, D, F)),
+        _ptr(shared_w1, "shared_w1", dt, (Fs, D)), _ptr(shared_w3, "shared_w3", dt, (Fs, D)),
+        _ptr(shared_w2, "shared_w2", dt, (D, Fs)),
+        top_k, float(scale), _ptr(out, "out", torch.float32, (T, D)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, top_k)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, top_k)), _stream())
+    _check(st, "glm_moe_forward_noalloc")
     return out
 
 

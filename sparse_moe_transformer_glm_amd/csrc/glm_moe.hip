@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -677,6 +678,48 @@ int glm_moe_trace_read(glm_moe_trace* trace, float* stage_ms, int* calls) {
   }
   *calls = trace->calls;
   return GLM_MOE_OK;
+}
+
+// Workspace of glm_moe_forward_noalloc: one array per GPU, resident until
+// the process ends.  Host code never uses the array's name as an address:
+// its device address comes from hipGetSymbolAddress, once per device.
+static constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+int glm_moe_forward_noalloc(const glm_moe_dims* d, const void* x, const float* router_w,
+                            const float* corr_bias, const void* w1, const void* w3, const void* w2,
+                            const void* shared_w1, const void* shared_w3, const void* shared_w2,
+                            int top_k, float scale, float* out, int32_t* topk_idx_out,
+                            float* topk_w_out, hipStream_t stream) {
+  Plan P;
+  int st = make_plan(d, top_k, nullptr, false, &P);
+  if (st) return st;
+  if (P.T == 0) return GLM_MOE_OK;
+  if (P.total > kScratchBytes)
+    return fail(GLM_MOE_EWORKSPACE,
+                "glm_moe_forward_noalloc: these sizes need %zu bytes of workspace, above its "
+                "fixed %zu-byte buffer (use glm_moe_forward with a workspace)",
+                P.total, kScratchBytes);
+  int dev = 0;
+  GLM_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GLM_MOE_EUNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return fail(GLM_MOE_EHIP, "hipGetSymbolAddress(scratch): %s",
+                hipGetErrorString(g_scratch_err[dev]));
+  return glm_moe_forward_ex(d, nullptr, x, router_w, corr_bias, w1, w3, w2, shared_w1, shared_w3,
+                            shared_w2, top_k, scale, out, topk_idx_out, topk_w_out,
+                            g_scratch_ptr[dev], kScratchBytes, stream, nullptr);
 }
 
 const char* glm_moe_status_string(int status) {
