@@ -63,6 +63,9 @@ constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
 #endif
 constexpr int32_t kSoleRowTile = 1 << 16;  // TileDesc::group flag
 constexpr int32_t kGroupMask = kSoleRowTile - 1;
+// TileDesc::group bits 20 and up: K chunk of a down tile of the shared (dense)
+// group when its contraction is split (DownArgs::ksplit > 1)
+constexpr int kKChunkShift = 20;
 constexpr int kCpolNt = 2;  // cache-policy immediate of the LDS-DMA load: NT
 template <int BM, int BN>
 constexpr bool kStreamB = BM <= GLM_STREAM_B_MAX_BM && BN >= 128;
@@ -121,6 +124,7 @@ struct ScanParams {
   int T, E, k, F, Fs, D;
   GemmShape gu, dn;
   int gu_desc_cap, dn_desc_cap;
+  int dn_ksplit;               // K chunks of the shared group's down tiles (1: whole K)
 };
 hipError_t launch_scan(const uint64_t* masks, const ScanParams& p,
                        int32_t* counts, int32_t* offsets, int32_t* tile_base,
@@ -166,8 +170,10 @@ struct DownArgs {
   const float* row_w;          // [T*k] routing weight of each expert-sorted row
   const TileDesc* desc;        // tiles of the routed groups and the shared expert (group E)
   const int32_t* desc_count;
-  float* Y;                    // [T][k+1][D]: slot j < k routed (weighted), slot k shared
+  float* Y;                    // [T][k+ksplit][D]: slot j < k routed (weighted), slots
+                               // k .. k+ksplit-1 the shared group's K chunks
   int T, D, E, F, Fs, k;
+  int ksplit;                  // K chunks of the shared group (only without routed groups)
   int grid;
   int xblk;
   int early;                   // two-stage tiles: issue each refill before the wait

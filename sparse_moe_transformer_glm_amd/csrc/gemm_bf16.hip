@@ -111,7 +111,8 @@ __device__ __forceinline__ const bf16_t* tile_row_src(const GateUpArgs& gu, cons
 //    per-wave LDS scratch of MB x TN/2 bf16, used when GU_LDS) one MB-row block
 //    at a time through LDS with 16-byte stores, else straight from the
 //    accumulators.
-//  * DOWN: Y[t][j] = w * acc to the row's (token, slot) place; `s_asg` /
+//  * DOWN: Y[t][j] = w * acc to the row's (token, slot) place (the shared
+//    group's K chunk kc to slot k + kc); `s_asg` /
 //    `s_wt` (BM entries each) take every row's Y row and weight; with `yblk`
 //    (a per-wave LDS scratch of MB x TN fp32, used when DN_LDS) through LDS
 //    with 16-byte stores.
@@ -120,7 +121,7 @@ __device__ __forceinline__ const bf16_t* tile_row_src(const GateUpArgs& gu, cons
 template <class C, int MODE, bool GU_LDS, bool DN_LDS, class Acc>
 __device__ __forceinline__ void tile_epilogue(const GateUpArgs& gu, const DownArgs& dn,
                                               Acc (&acc)[C::FM][C::FN], int g, int row0, int rows,
-                                              int col0, int wrow0, int live_m, int row_a,
+                                              int col0, int kc, int wrow0, int live_m, int row_a,
                                               float row_wt, bf16_t* hblk, float* yblk, int* s_asg,
                                               float* s_wt) {
   constexpr int MB = C::MB, FM = C::FM, FN = C::FN, TN = C::TN, WN = C::WN;
@@ -185,8 +186,9 @@ __device__ __forceinline__ void tile_epilogue(const GateUpArgs& gu, const DownAr
   } else {
     __syncthreads();  // every wave is done reading the stages (s_asg may alias one)
     // row of Y and routing weight of every row of the tile
-    if (tid < rows) {
-      s_asg[tid] = g == dn.E ? (row0 + tid) * (dn.k + 1) + dn.k : y_row(row_a, dn.k);
+    if (tid < rows) {  // the shared group's K chunk kc writes slot k + kc
+      s_asg[tid] = g == dn.E ? (row0 + tid) * (dn.k + dn.ksplit) + dn.k + kc
+                             : y_row(row_a, dn.k);
       s_wt[tid] = row_wt;
     }
     __syncthreads();  // the row table is complete
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   const int wm = wave / WN, wn = wave % WN;
 
   // ---------------------------------------------------------- tile setup
-  int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0;
+  int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0, kc = 0, koff = 0;
   bool sole = false;
   if constexpr (MODE == GATE_UP) {
     const int i = xcd_tile(*gu.desc_count, gu.xblk);
@@ -277,7 +279,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     const TileDesc d = dn.desc[i];
     g = d.group & kGroupMask; sole = d.group & kSoleRowTile; row0 = d.row0; rows = d.rows;
     col0 = d.col0;
-    K = (g == dn.E) ? dn.Fs : dn.F;
+    K = dn.F;
+    if (g == dn.E) {  // the shared group, possibly one K chunk of it
+      kc = d.group >> kKChunkShift;
+      K = dn.Fs / dn.ksplit;
+      koff = kc * K;
+    }
   }
 
   // DMA sources: instruction q = wave + i*NW covers rows [q*RPI, q*RPI+RPI) of
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     const int q = wave + i * NW;
     const int r = q * RPI + lane / CPR;
     const int ch = (lane % CPR) ^ swz<BK>(r);
-    src[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + ch * 8;
+    src[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff + ch * 8;
   }
 
   // Per-row data of the down epilogue (assignment and routing weight of row
@@ -327,10 +334,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     }
   };
 
-  // rows of this tile handled by each wave row: an even split in MB blocks
-  const int per = min(TM, ((rows + C::WM - 1) / C::WM + MB - 1) / MB * MB);
-  const int wrow0 = wm * per;
-  const int live_m = min(min(FM, per / MB), max(0, (rows - wrow0 + MB - 1) / MB));
+  // MFMA row blocks holding valid rows, dealt to the wave rows in turn as
+  // evenly as possible: a SIMD runs one wave of each wave row, so its MFMA
+  // work is the blocks of both (ceil(rows / MB) in all, not WM x the larger)
+  const int nb = (rows + MB - 1) / MB;
+  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
+  const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
 
   // fragment read offsets (elements, without the stage base and k-chunk)
   const int lr = lane % MB, lk = lane / MB;
@@ -481,7 +490,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   constexpr bool GU_LDS = NW * MB * HC * 2 <= C::STAGE * 2 && HC % 8 == 0 &&
                           MB % (kWave / (HC / 8 > 0 ? HC / 8 : 1)) == 0;
   constexpr bool DN_LDS = NW * MB * TN * 4 <= C::STAGE * 2;
-  tile_epilogue<C, MODE, GU_LDS, DN_LDS>(gu, dn, acc, g, row0, rows, col0, wrow0, live_m, row_a, row_wt,
+  tile_epilogue<C, MODE, GU_LDS, DN_LDS>(gu, dn, acc, g, row0, rows, col0, kc, wrow0, live_m,
+                                         row_a, row_wt,
                          GU_LDS ? lds0 + wave * (MB * HC) : nullptr,
                          DN_LDS ? reinterpret_cast<float*>(lds0) + wave * (MB * TN) : nullptr,
                          s_asg, s_wt);
@@ -498,7 +508,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
 // barrier per step.  Each slot is its own LDS object, so the compiler tracks
 // the LDS-DMA copies per slot.  Rows are 128-byte pieces (K step 64): a
 // narrower step would issue two requests per cache line.
-template <class C, int MODE>
+template <class C, int MODE, int NA, int NB>
 __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownArgs dn) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MB = C::MB;
   constexpr int WN = C::WN, NW = C::NW, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
@@ -511,17 +521,19 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
                     2 * BM * 4 <= BM * BK * 2,
                 "epilogue scratch fits the ring slots");
 
-  __shared__ __attribute__((aligned(1024))) bf16_t la0[BM * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t la1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t lb0[BN * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t lb1[BN * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t lb2[BN * BK];
+  static_assert(BM == BN && NA + NB == 5 && NA >= 2 && NB >= 2 && NA != NB,
+                "five equal slots: the A ring takes NA, the B ring NB");
+  __shared__ __attribute__((aligned(1024))) bf16_t ls0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t ls1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t ls2[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t ls3[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t ls4[BM * BK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0;
+  int g = 0, row0 = 0, rows = 0, col0 = 0, K = 0, kc = 0, koff = 0;
   if constexpr (MODE == GATE_UP) {
     const int i = xcd_tile(*gu.desc_count, gu.xblk);
     if (i < 0) return;
@@ -532,7 +544,12 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     if (i < 0) return;
     const TileDesc d = dn.desc[i];
     g = d.group & kGroupMask; row0 = d.row0; rows = d.rows; col0 = d.col0;
-    K = (g == dn.E) ? dn.Fs : dn.F;
+    K = dn.F;
+    if (g == dn.E) {  // the shared group, possibly one K chunk of it
+      kc = d.group >> kKChunkShift;
+      K = dn.Fs / dn.ksplit;
+      koff = kc * K;
+    }
   }
 
   // copy i of a wave covers operand rows (wave + i*NW)*RPI .. +RPI of a slot;
@@ -542,13 +559,13 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
 #pragma unroll
   for (int i = 0; i < AW; ++i) {
     const int r = (wave + i * NW) * RPI + lane / CPR;
-    sa[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) +
+    sa[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff +
             ((lane % CPR) ^ swz<BK>(r)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < BW; ++i) {
     const int n = (wave + i * NW) * RPI + lane / CPR;
-    sb[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, BM + n) +
+    sb[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, BM + n) + koff +
             ((lane % CPR) ^ swz<BK>(n)) * 8;
   }
 
@@ -562,8 +579,11 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     }
   }
 
-  auto a_slot = [&](int s) -> bf16_t* { return s == 0 ? la0 : la1; };
-  auto b_slot = [&](int s) -> bf16_t* { return s == 0 ? lb0 : s == 1 ? lb1 : lb2; };
+  auto slot = [&](int i) -> bf16_t* {
+    return i == 0 ? ls0 : i == 1 ? ls1 : i == 2 ? ls2 : i == 3 ? ls3 : ls4;
+  };
+  auto a_slot = [&](int s) -> bf16_t* { return slot(s); };
+  auto b_slot = [&](int s) -> bf16_t* { return slot(NA + s); };
   auto issueA = [&](bf16_t* st, int kt) {
 #pragma unroll
     for (int i = 0; i < AW; ++i)
@@ -578,39 +598,55 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   };
 
   const int nk = K / BK;
-  // A rows of steps 0 and 1 and B rows of steps 0..2, in step order; wait
-  // for step 0
-  auto prologue = [&]() {
-    issueA(la0, 0);
-    issueB(lb0, 0);
-    if (nk > 1) {
-      issueA(la1, 1);
-      issueB(lb1, 1);
+  // The shallower ring's copies of a step are issued before the deeper
+  // ring's: then at the end of step kt the only copies issued after step
+  // kt+1's are the deeper ring's copies of step kt+2.
+  constexpr bool A_FIRST = NA < NB;
+  constexpr int DEEP_W = A_FIRST ? BW : AW;
+  constexpr int NMAX = NA > NB ? NA : NB;
+  auto issue_step = [&](int st) {  // the copies of step st in the prologue
+    if (A_FIRST) {
+      if (st < NA) issueA(a_slot(st), st);
+      if (st < NB) issueB(b_slot(st), st);
+    } else {
+      if (st < NB) issueB(b_slot(st), st);
+      if (st < NA) issueA(a_slot(st), st);
     }
+  };
+  // Steps 0 .. NMAX-1 in step order; wait for step 0
+  auto prologue = [&]() {
+    issue_step(0);
+    if (nk > 1) issue_step(1);
     if (nk > 2) {
-      issueB(lb2, 2);
-      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(AW + 2 * BW));
+      issue_step(2);
+      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(AW + BW + (NA > 2 ? AW : 0) + (NB > 2 ? BW : 0)));
     } else {
       __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     }
     lds_barrier();
   };
-  // End of step kt: the copies issued after step kt+1's are at most the B
-  // rows of step kt+2; wait for step kt+1, barrier, refill step kt's slots.
-  // STEADY: steps kt+1 .. kt+3 exist (known at compile time).
+  // End of step kt: wait for step kt+1 (the deeper ring's copies of step
+  // kt+2 may stay in flight), barrier, refill the slots step kt used.
+  // STEADY: steps kt+1 .. kt+NMAX exist (known at compile time).
   auto handover = [&](auto sc, int kt, auto steady_c) {
     constexpr int u = decltype(sc)::value;  // kt % 6
     constexpr bool STEADY = decltype(steady_c)::value;
-    if (STEADY || kt + 2 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(BW));
+    if (STEADY || kt + 2 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(DEEP_W));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
-    if (STEADY || kt + 2 < nk) issueA(a_slot(u % 2), kt + 2);
-    if (STEADY || kt + 3 < nk) issueB(b_slot(u % 3), kt + 3);
+    if (A_FIRST) {
+      if (STEADY || kt + NA < nk) issueA(a_slot(u % NA), kt + NA);
+      if (STEADY || kt + NB < nk) issueB(b_slot(u % NB), kt + NB);
+    } else {
+      if (STEADY || kt + NB < nk) issueB(b_slot(u % NB), kt + NB);
+      if (STEADY || kt + NA < nk) issueA(a_slot(u % NA), kt + NA);
+    }
   };
 
-  const int per = min(TM, ((rows + C::WM - 1) / C::WM + MB - 1) / MB * MB);
-  const int wrow0 = wm * per;
-  const int live_m = min(min(FM, per / MB), max(0, (rows - wrow0 + MB - 1) / MB));
+  // MFMA row blocks dealt to the wave rows as evenly as possible (see above)
+  const int nb = (rows + MB - 1) / MB;
+  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
+  const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
   const int lr = lane % MB, lk = lane / MB;
   const int sw = swz<BK>(lr);
 
@@ -645,20 +681,20 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
                                                               acc[m][n], 0, 0, 0);
     };
     prologue();
-    load_frags(la0, lb0, 0, 0);
+    load_frags(a_slot(0), b_slot(0), 0, 0);
     // one K step on the slots of step kt (u = kt % 6); the hand-over sits
     // before the last sub-step's MFMAs, which cover the next slots' first reads
     auto step = [&](auto sc, int kt, auto steady_c) {
       constexpr int u = decltype(sc)::value;
       constexpr bool STEADY = decltype(steady_c)::value;
-      const bf16_t* ca = a_slot(u % 2);
-      const bf16_t* cb = b_slot(u % 3);
+      const bf16_t* ca = a_slot(u % NA);
+      const bf16_t* cb = b_slot(u % NB);
 #pragma unroll
       for (int sub = 0; sub < C::KSUB; ++sub) {
         if (sub + 1 < C::KSUB) load_frags(ca, cb, sub + 1, (sub + 1) & 1);
         if (sub == C::KSUB - 1 && (STEADY || kt + 1 < nk)) {
           handover(sc, kt, steady_c);
-          load_frags(a_slot((u + 1) % 2), b_slot((u + 1) % 3), 0, 0);
+          load_frags(a_slot((u + 1) % NA), b_slot((u + 1) % NB), 0, 0);
         }
         // keep the reads issued above ahead of this sub-step's MFMAs
         __builtin_amdgcn_sched_barrier(0);
@@ -666,7 +702,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
       }
     };
     int kt = 0;
-    for (; kt + 8 < nk; kt += 6)  // every step of the group has three steps after it
+    for (; kt + 5 + NMAX < nk; kt += 6)  // every step of the group has NMAX steps after it
       unroll<6>([&](auto uc) { step(uc, kt + decltype(uc)::value, std::true_type{}); });
     for (; kt < nk; kt += 6)
       unroll<6>([&](auto uc) {
@@ -693,12 +729,12 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     }
   }
 
-  // epilogue scratch in the ring slots (no copy is in flight any more):
-  // hidden blocks in la0, the row table in la1, fp32 blocks in lb0 / lb1
+  // epilogue scratch in the slots (no copy is in flight any more): hidden
+  // blocks in slot 0, the row table in slot 1, fp32 blocks in slots 2 and 3
   tile_epilogue<C, MODE, true, true>(
-      gu, dn, acc, g, row0, rows, col0, wrow0, live_m, row_a, row_wt, la0 + wave * (MB * HC),
-      reinterpret_cast<float*>(wave < NW / 2 ? lb0 : lb1) + (wave % (NW / 2)) * (MB * TN),
-      reinterpret_cast<int*>(la1), reinterpret_cast<float*>(la1) + BM);
+      gu, dn, acc, g, row0, rows, col0, kc, wrow0, live_m, row_a, row_wt, ls0 + wave * (MB * HC),
+      reinterpret_cast<float*>(wave < NW / 2 ? ls2 : ls3) + (wave % (NW / 2)) * (MB * TN),
+      reinterpret_cast<int*>(ls1), reinterpret_cast<float*>(ls1) + BM);
 }
 
 // out[t][d] = Y[t][k][d] + Y[t][0][d] + ... + Y[t][k-1][d] (+ residual[t][d]),
@@ -762,11 +798,14 @@ using CfgNarrow = Cfg<32, 64, 64, 1, 2, 4, 16>;    // widths that are not a mult
 #ifndef GLM_SPLIT_BIG
 #define GLM_SPLIT_BIG 1
 #endif
+#ifndef GLM_SPLIT_NA  // activation slots of the split rings (the weight ring has the rest of 5)
+#define GLM_SPLIT_NA 2
+#endif
 template <class C, int MODE>
 hipError_t launch_one(const GateUpArgs& gu, const DownArgs& dn, unsigned grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   if constexpr (C::BM == 256 && C::BN == 256 && C::BK == 64 && C::MB == 32 && GLM_SPLIT_BIG) {
-    split_gemm_kernel<C, MODE><<<grid, C::NT, 0, s>>>(gu, dn);
+    split_gemm_kernel<C, MODE, GLM_SPLIT_NA, 5 - GLM_SPLIT_NA><<<grid, C::NT, 0, s>>>(gu, dn);
     return hipGetLastError();
   }
   if constexpr (C::ST == 2) {

@@ -266,9 +266,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
   };
   constexpr int VPS = IPW + SPW;  // DMA instructions per wave per stage
 
-  const int per = min(TM, ((rows + C::WM - 1) / C::WM + 31) / 32 * 32);
-  const int wrow0 = wm * per;
-  const int live_m = min(min(FM, per / 32), max(0, (rows - wrow0 + 31) / 32));
+  // 32-row MFMA blocks holding valid rows, dealt to the wave rows as evenly
+  // as possible (a SIMD runs one wave of each wave row)
+  const int nb = (rows + 31) / 32;
+  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
+  const int wrow0 = 32 * (wm * (nb / C::WM) + min(wm, nb % C::WM));
 
   const int lr = lane % 32, lg = lane / 32;
   const int sw = swz(lr);

@@ -39,6 +39,7 @@ struct Plan {
   int ksplit, kchunk;
   GemmShape gu, dn;
   int gu_cap, dn_cap;
+  int dn_ksplit;     // K chunks of the shared (dense) group's down tiles
   GroupRouting gr;
   const float* norm_weight;
   float norm_eps;
@@ -145,23 +146,34 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
     P.ksplit = cdiv(P.D, P.kchunk);
     const double per_group = dense ? (double)T : (double)A / P.E;
     const bool wide_gu = (dense || P.F % 128 == 0) && P.Fs % 128 == 0;
+    const bool wide_dn = P.D % 256 == 0;
     // A dense layer on a decode-size batch is a single group of a few rows:
-    // the 128 x 256 tiles would leave most CUs idle (144 tiles at width
-    // 18432, 24 in the down projection), the 32 x 64 tiles give 4x more.
+    // its weights are streamed on the decode tiles (32 x 128), and the down
+    // projection, whose few column tiles would leave most CUs idle (96 tiles
+    // at 64 tokens and hidden 6144), splits its contraction into K chunks
+    // that write separate slots of Y, summed in order by the combine.
     const bool few_tiles = dense && per_group <= 96.0;
-    P.gu = mx ? gemm_shape_mx(per_group, wide_gu && !few_tiles)
-              : gemm_shape(per_group, wide_gu && !few_tiles);
-    P.dn = mx ? gemm_shape_mx(per_group, P.D % 256 == 0 && !few_tiles)
-              : gemm_shape(per_group, P.D % 256 == 0 && !few_tiles);
+    P.gu = mx ? gemm_shape_mx(per_group, wide_gu) : gemm_shape(few_tiles ? 1.0 : per_group, wide_gu);
+    P.dn = mx ? gemm_shape_mx(per_group, wide_dn) : gemm_shape(few_tiles ? 1.0 : per_group, wide_dn);
+    P.dn_ksplit = 1;
+    if (few_tiles && T > 0) {
+      const int tiles = cdiv(T, P.dn.BM) * (P.D / P.dn.BN);
+      const int ksteps = P.Fs / 64;
+      int ks = cdiv(512, tiles);
+      if (ks > ksteps / 16) ks = ksteps / 16;  // chunks of at least 16 K steps
+      while (ks > 1 && ksteps % ks) --ks;      // whole K steps per chunk
+      P.dn_ksplit = ks < 1 ? 1 : ks;
+    }
     // tile-list capacity: routed tiles plus the shared (or dense) group's (group E)
     P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) +
                cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
     P.dn_cap = (dense ? 0 : desc_cap(A, P.E, P.dn, P.D / P.dn.BN)) +
-               cdiv(T, P.dn.BM) * (P.D / P.dn.BN);
+               cdiv(T, P.dn.BM) * (P.D / P.dn.BN) * P.dn_ksplit;
   } else {
     P.ksplit = 1; P.kchunk = P.D;
     P.gu = P.dn = GemmShape{0, 0};
     P.gu_cap = P.dn_cap = 0;
+    P.dn_ksplit = 1;
   }
 
   const size_t act = bf16 ? 2 : 4;
@@ -184,7 +196,8 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   P.row_w = take((size_t)A * 4);
   P.H = take((size_t)A * P.F * hid);
   P.Hs = take((size_t)T * P.Fs * hid);
-  P.Y = take((size_t)T * (P.k + 1) * P.D * 4);  // [T][k+1][D], slot k: shared expert
+  // [T][k+ks][D]: slots k .. k+ks-1 hold the shared expert (ks K chunks)
+  P.Y = take((size_t)T * (P.k + P.dn_ksplit) * P.D * 4);
   P.xq = take(mx ? (size_t)T * P.D : 0);        // MXFP8 input codes and scales
   P.xs = take(mx ? (size_t)T * P.D / 32 : 0);
   P.xsp = take(mx ? (size_t)A * P.D / 32 : 0);  // input scales in expert-row order
@@ -308,6 +321,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   sp.dn = P.bf16 ? P.dn : GemmShape{16, 128};
   sp.gu_desc_cap = P.gu_cap;
   sp.dn_desc_cap = P.dn_cap;
+  sp.dn_ksplit = P.dn_ksplit;
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCAN));
   GLM_HIP(launch_scan(masks, sp, counts, offsets, tile_base, gu_desc, gu_count, dn_desc, dn_count, s));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));
@@ -371,6 +385,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     da.w2 = static_cast<const bf16_t*>(w2); da.sw2 = static_cast<const bf16_t*>(shared_w2);
     da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
+    da.ksplit = P.dn_ksplit;
     da.xblk = P.dn.BM == 32 ? kXcdBlockDecodeDn : kXcdBlock;
     da.early = ga.early;  // same two-stage ring, same fill rule
     da.grid = xcd_grid(P.dn_cap, da.xblk);
@@ -378,7 +393,8 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     GLM_HIP(launch_down_bf16(da, P.dn, s));
 
     GLM_HIP(rec.mark(GLM_MOE_STAGE_SHARED_COMBINE));
-    GLM_HIP(launch_combine(Y, out, P.T, P.D, P.k, residual, true, s));
+    // every slot of Y, in order (the shared expert's K chunks included)
+    GLM_HIP(launch_combine(Y, out, P.T, P.D, P.k + P.dn_ksplit - 1, residual, true, s));
   } else {
     F32Args fa{};
     fa.x = static_cast<const float*>(xin);

@@ -58,7 +58,7 @@ __device__ inline int tile_row0(int m, int mt, int rows, int gran) {
 // previous round's last position, a few LDS reads per round.
 __device__ inline void write_descs(const int* pos, const int* og, int total, const int* cnt,
                                    const int* off, int T, int E, int BM, int shared_nt,
-                                   int col_w, TileDesc* __restrict__ out) {
+                                   int col_w, int ksplit, TileDesc* __restrict__ out) {
   constexpr int kWaves = kScanThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int chunk = cdiv(cdiv(total, kWaves), kWave) * kWave;
@@ -78,20 +78,24 @@ __device__ inline void write_descs(const int* pos, const int* og, int total, con
     const int g = og[l];
     const int rows = g < E ? cnt[g] : T;
     const int mt = cdiv(rows, BM);
-    int nt, m, r0, rt;
+    int nt, m, r0, rt, kc = 0;
     if (mt == 1 && g < E) {  // one row tile (the common case): no divisions
       m = 0;
       nt = i - pos[l];
       r0 = 0;
       rt = rows;
     } else {
-      tile_order(i - pos[l], mt, shared_nt, g == E, &m, &nt);
+      // the shared group's K chunks count as extra column tiles (chunk innermost)
+      const int ks = g == E ? ksplit : 1;
+      tile_order(i - pos[l], mt, shared_nt * ks, g == E, &m, &nt);
       const int gran = min(64, BM);
       r0 = tile_row0(m, mt, rows, gran);
       rt = tile_row0(m + 1, mt, rows, gran) - r0;
+      kc = nt % ks;
+      nt /= ks;
     }
     TileDesc d;
-    d.group = g | (mt == 1 ? kSoleRowTile : 0);
+    d.group = g | (mt == 1 ? kSoleRowTile : 0) | (kc << kKChunkShift);
     d.row0 = (g < E ? off[g] : 0) + r0;
     d.rows = rt;
     d.col0 = nt * col_w;
@@ -187,7 +191,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     }
     // the shared expert is group E of both GEMMs, over every token
     s_gu[E + 1] = min(s_gu[E] + cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN), p.gu_desc_cap);
-    s_dn[E + 1] = min(s_dn[E] + cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN), p.dn_desc_cap);
+    s_dn[E + 1] = min(s_dn[E] + cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) * p.dn_ksplit,
+                      p.dn_desc_cap);
   }
   __syncthreads();
 
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     if (lpt_d) {
       const int rd = s_rank[2][tid];
       s_od[1 + rd] = tid;
-      s_pd[1 + rd] = cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) + s_rank[3][tid];
+      s_pd[1 + rd] = cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) * p.dn_ksplit + s_rank[3][tid];
     } else {
       s_od[tid] = tid;
       s_pd[tid] = s_dn[tid];
@@ -279,9 +284,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
   // tile descriptors: groups in listing order, then output-column tile, then row tile
   write_descs(s_pg, s_og, s_gu[E + 1], s_cnt, s_off, p.T, E, p.gu.BM, 2 * p.Fs / p.gu.BN,
-              p.gu.BN / 2, gu_desc);
+              p.gu.BN / 2, 1, gu_desc);
   write_descs(s_pd, s_od, s_dn[E + 1], s_cnt, s_off, p.T, E, p.dn.BM, p.D / p.dn.BN, p.dn.BN,
-              dn_desc);
+              p.dn_ksplit, dn_desc);
 }
 
 // One wave per 64-token tile.  A token's rank among the tile's tokens of
