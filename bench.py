@@ -51,6 +51,61 @@ def measured_traffic(kind):
     return d[kind]["hbm_bytes_per_launch"]
 
 
+def measured_peaks(torch):
+    """Hardware ceilings measured on this GPU before the layer runs
+    (libglm_peaks.so): bf16 and fp8 MFMA loops with the shader clock each
+    observed, and a streaming read of 8 GiB (far above the last-level cache)."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_transformer_glm_amd", "libglm_peaks.so"))
+    vp, i32, f32p, f64p = (ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                           ctypes.POINTER(ctypes.c_double))
+    L.glm_peak_mfma.argtypes = [i32, i32, i32, vp, f32p, f64p, f64p, vp]
+    L.glm_peak_hbm_read.argtypes = [vp, ctypes.c_size_t, i32, vp, f32p, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    scratch = torch.empty(16 + 4096 * 256 * 4, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, fp8 in (("bf16", 0), ("fp8", 1)):
+        ms, flops, mhz = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
+        st = L.glm_peak_mfma(fp8, 100000, 2, scratch.data_ptr(), ctypes.byref(ms),
+                             ctypes.byref(flops), ctypes.byref(mhz), stream)
+        if st != 0:
+            raise RuntimeError(f"glm_peak_mfma({name}) failed: hipError {st}")
+        res[f"mfma_{name}_tflops"] = round(flops.value / (ms.value * 1e-3) / 1e12, 1)
+        res[f"mfma_{name}_clock_mhz"] = round(mhz.value, 0)
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ms = ctypes.c_float()
+    st = L.glm_peak_hbm_read(buf.data_ptr(), nbytes, 5, scratch.data_ptr(), ctypes.byref(ms),
+                             stream)
+    if st != 0:
+        raise RuntimeError(f"glm_peak_hbm_read failed: hipError {st}")
+    res["hbm_read_gbs"] = round(nbytes / (ms.value * 1e-3) / 1e9, 1)
+    res["hbm_read_bytes"] = nbytes
+    del buf, scratch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+PEAKS = None  # measured ceilings of this run (main sets it)
+
+
+def with_measured(roof, peaks=None):
+    """Add the fraction of the measured ceiling to a roofline object."""
+    peaks = peaks or PEAKS
+    if not peaks:
+        return roof
+    if roof["bound"] == "hbm":
+        m = peaks["hbm_read_gbs"]
+    elif roof["peak"] == PEAK_FP8_TFLOPS:
+        m = peaks["mfma_fp8_tflops"]
+    else:
+        m = peaks["mfma_bf16_tflops"]
+    roof["measured_peak"] = m
+    roof["frac_measured"] = round(roof["achieved"] / m, 4)
+    return roof
+
+
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -188,7 +243,7 @@ def record(w, elapsed, steps, per_call, counts, bound, traffic_kind=None):
              "flops": lf, "bytes": lb}
     load = {"active_experts": n_active, "max_rows": int(counts.max()),
             "mean_rows": round(float(counts.mean()), 2), "min_rows": int(counts.min())}
-    return ms, roof, layer, load
+    return ms, with_measured(roof), layer, load
 
 
 def dense_record(glm, torch, w, F, dw, steps, warmup, ws, bound):
@@ -221,7 +276,7 @@ def dense_record(glm, torch, w, F, dw, steps, warmup, ws, bound):
                 "work_per_launch": b[dom], "avg_launch_ms": round(pc[dom], 4)}
     return {"workload": f"dense FFN hidden {D} width {F}, {T} tokens", "tokens": T,
             "value": round(T * steps / elapsed, 1), "unit": "tokens/s", "steps": steps,
-            "ms_per_step": round(ms, 4), "roofline": roof,
+            "ms_per_step": round(ms, 4), "roofline": with_measured(roof),
             "stages_ms": {s: round(v, 4) for s, v in pc.items() if v > 0}}
 
 
@@ -391,6 +446,8 @@ def main():
                     help="skip the block / group-routing / dense-FFN measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the MFMA / HBM ceiling microbenchmarks (profiling runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -408,6 +465,11 @@ def main():
     from workloads.device import stream_layer, to_device
 
     torch.cuda.set_device(0)
+    global PEAKS
+    peaks = None
+    if args.peaks:
+        peaks = PEAKS = measured_peaks(torch)
+        log(f"measured ceilings: {peaks}")
     wp = wl.WORKLOADS[args.workload]
     t0 = time.time()
     log(f"drawing + uploading {wp.name} layer weights (seeded, bf16)")
@@ -441,6 +503,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof, "layer_roofline": layer, "routing_load": load,
         "stages_ms": stages(per_call), "call_ms": per_call["_pct"], "route_ms": route_ms,
+        "measured_peaks": peaks,
     }
 
     if wd:

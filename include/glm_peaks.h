@@ -1,0 +1,47 @@
+/* Measured hardware ceilings of the GPU (libglm_peaks.so).
+ *
+ * Not part of the MoE layer: two microbenchmarks whose rates the benchmark
+ * reports beside the published MI355X peaks, so that each kernel's roofline
+ * fraction can also be read against what the chip sustains at the clock it
+ * actually ran.  Both run on the calling thread's current HIP device, on
+ * `stream`, and block until their timed launches have finished.
+ *
+ * Return value: a hipError_t value, 0 on success; hipErrorInvalidValue (1)
+ * for a null pointer, a non-positive count or a misaligned size.
+ */
+#ifndef GLM_PEAKS_H
+#define GLM_PEAKS_H
+
+#include <stddef.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Dense MFMA throughput.  `blocks_per_cu` workgroups of four waves per compute
+ * unit; every wave issues `iters` x 8 independent register-to-register MFMAs:
+ * v_mfma_f32_32x32x16_bf16 when fp8 == 0, the block-scaled
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands with unit scales when
+ * fp8 == 1.  Outputs (host pointers): *ms the timed launch (HIP events),
+ * *flops the floating-point operations it performed (2 per multiply-add),
+ * *clock_mhz the shader clock one wave observed over its loop.
+ * `scratch`: caller-owned device buffer of at least
+ * 16 + 4 * 256 * blocks_per_cu * (number of compute units) bytes. */
+int glm_peak_mfma(int fp8, int iters, int blocks_per_cu, void* scratch, float* ms,
+                  double* flops, double* clock_mhz, hipStream_t stream);
+
+/* Streaming HBM read bandwidth.  Reads `bytes` (a multiple of 16) from the
+ * device buffer `src` (16-byte aligned; make it far larger than the 256 MB
+ * last-level cache) with 16-byte non-temporal loads, once untimed and then
+ * `reps` timed times; *ms (host pointer) receives the fastest launch.
+ * `scratch`: caller-owned device buffer of at least 2048 * 256 * 4 bytes. */
+int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, float* ms,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLM_PEAKS_H */

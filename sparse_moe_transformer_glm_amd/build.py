@@ -1,4 +1,5 @@
-"""Build ``libglm_moe.so`` (HIP, gfx950 only) in-tree with hipcc.
+"""Build ``libglm_moe.so`` (the layer, HIP, gfx950 only) and ``libglm_peaks.so``
+(the hardware-ceiling microbenchmarks that ``bench.py`` runs) in-tree with hipcc.
 
 Usage: ``python -m sparse_moe_transformer_glm_amd.build``.  Every call
 recompiles; objects go to ``_build/`` at the repository root.
@@ -17,6 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libglm_moe.so")
 SOURCES = ["router.hip", "permute.hip", "gemm_bf16.hip", "gemm_mx.hip", "gemm_f32.hip",
            "block.hip", "glm_moe.hip"]
+PEAKS_LIB = os.path.join(PKG, "libglm_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 
@@ -47,18 +50,21 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     build_dir = os.path.join(ROOT, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    objs, cmds = [], []
-    for src in SOURCES:
-        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-        objs.append(obj)
-        cmds.append([hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+    libs = ((LIB, SOURCES), (PEAKS_LIB, PEAKS_SOURCES))
+    cmds, objs = [], {}
+    for lib, sources in libs:
+        for src in sources:
+            obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+            objs.setdefault(lib, []).append(obj)
+            cmds.append([hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 1)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for lib, _ in libs:
+        tmp = lib + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs[lib], "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -54,6 +54,19 @@ def test_no_undefined_internal_symbols():
     assert not bad, bad
 
 
+def test_peaks_library_exports_its_header():
+    """The ceiling microbenchmarks live in a library of their own with their own header."""
+    from sparse_moe_transformer_glm_amd import build as B
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "glm_peaks.h")).read(),
+                  flags=re.S)
+    declared = sorted(set(re.findall(r"\b(glm_peak_\w+)\s*\(", text)))
+    assert declared == ["glm_peak_hbm_read", "glm_peak_mfma"]
+    out = subprocess.run(["nm", "-D", "--defined-only", B.PEAKS_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (glm_\w+)", out))
+    assert exported == set(declared), exported
+
+
 def _ws(T, D, E, F, Fs, k, dt=glm.BF16):
     n = ctypes.c_size_t(0)
     st = glm.lib().glm_moe_workspace_size(ctypes.byref(Dims(T, D, E, F, Fs, dt, dt)), k,
