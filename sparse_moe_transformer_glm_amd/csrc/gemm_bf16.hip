@@ -552,16 +552,29 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     }
   }
 
-  // copy i of a wave covers operand rows (wave + i*NW)*RPI .. +RPI of a slot;
-  // lane l fills physical chunk l % CPR of its row, logical chunk (l % CPR) ^ swz
-  const bf16_t* sa[AW];
-  const bf16_t* sb[BW];
+  // MFMA row blocks dealt to the wave rows as evenly as possible: a SIMD
+  // runs one wave of each wave row, so its MFMA work is the blocks of both
+  const int nb = (rows + MB - 1) / MB;
+  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
+  const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
+
+  // A copies: wave (wm, wn) fills rows wn*RPI .. +RPI of each MFMA row block
+  // of its wave row, so it makes exactly one A copy per live block and rows
+  // of blocks past the valid rows are never fetched (the LDS rows they would
+  // fill reach only output rows that the epilogue drops).  B copy i of a wave
+  // covers rows (wave + i*NW)*RPI .. +RPI.  Lane l fills physical chunk
+  // l % CPR of its row, logical chunk (l % CPR) ^ swz.
+  static_assert(C::WN * RPI == MB, "the waves of a wave row cover one row block per copy");
+  const bf16_t* sa[FM];
+  int a_dst[FM];
 #pragma unroll
-  for (int i = 0; i < AW; ++i) {
-    const int r = (wave + i * NW) * RPI + lane / CPR;
+  for (int i = 0; i < FM; ++i) {
+    a_dst[i] = min(wrow0 + i * MB, BM - MB) + wn * RPI;
+    const int r = a_dst[i] + lane / CPR;
     sa[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff +
             ((lane % CPR) ^ swz<BK>(r)) * 8;
   }
+  const bf16_t* sb[BW];
 #pragma unroll
   for (int i = 0; i < BW; ++i) {
     const int n = (wave + i * NW) * RPI + lane / CPR;
@@ -584,11 +597,13 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   };
   auto a_slot = [&](int s) -> bf16_t* { return slot(s); };
   auto b_slot = [&](int s) -> bf16_t* { return slot(NA + s); };
-  auto issueA = [&](bf16_t* st, int kt) {
+  // LIVE: the wave row's live blocks (compile time), the wave's A copies per step
+  auto issueA = [&](auto live_c, bf16_t* st, int kt) {
+    constexpr int LIVE = decltype(live_c)::value;
 #pragma unroll
-    for (int i = 0; i < AW; ++i)
+    for (int i = 0; i < LIVE; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(sa[i] + (size_t)kt * BK),
-                                       (lds_void*)(st + (wave + i * NW) * (RPI * BK)), 16, 0, 0);
+                                       (lds_void*)(st + a_dst[i] * BK), 16, 0, 0);
   };
   auto issueB = [&](bf16_t* st, int kt) {
 #pragma unroll
@@ -602,24 +617,25 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   // ring's: then at the end of step kt the only copies issued after step
   // kt+1's are the deeper ring's copies of step kt+2.
   constexpr bool A_FIRST = NA < NB;
-  constexpr int DEEP_W = A_FIRST ? BW : AW;
   constexpr int NMAX = NA > NB ? NA : NB;
-  auto issue_step = [&](int st) {  // the copies of step st in the prologue
+  auto issue_step = [&](auto live_c, int st) {  // the copies of step st in the prologue
     if (A_FIRST) {
-      if (st < NA) issueA(a_slot(st), st);
+      if (st < NA) issueA(live_c, a_slot(st), st);
       if (st < NB) issueB(b_slot(st), st);
     } else {
       if (st < NB) issueB(b_slot(st), st);
-      if (st < NA) issueA(a_slot(st), st);
+      if (st < NA) issueA(live_c, a_slot(st), st);
     }
   };
   // Steps 0 .. NMAX-1 in step order; wait for step 0
-  auto prologue = [&]() {
-    issue_step(0);
-    if (nk > 1) issue_step(1);
+  auto prologue = [&](auto live_c) {
+    constexpr int AWL = decltype(live_c)::value;
+    issue_step(live_c, 0);
+    if (nk > 1) issue_step(live_c, 1);
     if (nk > 2) {
-      issue_step(2);
-      __builtin_amdgcn_s_waitcnt(GLM_VMCNT(AW + BW + (NA > 2 ? AW : 0) + (NB > 2 ? BW : 0)));
+      issue_step(live_c, 2);
+      __builtin_amdgcn_s_waitcnt(
+          GLM_VMCNT(AWL + BW + (NA > 2 ? AWL : 0) + (NB > 2 ? BW : 0)));
     } else {
       __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     }
@@ -628,25 +644,22 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   // End of step kt: wait for step kt+1 (the deeper ring's copies of step
   // kt+2 may stay in flight), barrier, refill the slots step kt used.
   // STEADY: steps kt+1 .. kt+NMAX exist (known at compile time).
-  auto handover = [&](auto sc, int kt, auto steady_c) {
+  auto handover = [&](auto live_c, auto sc, int kt, auto steady_c) {
     constexpr int u = decltype(sc)::value;  // kt % 6
     constexpr bool STEADY = decltype(steady_c)::value;
+    constexpr int DEEP_W = A_FIRST ? BW : decltype(live_c)::value;
     if (STEADY || kt + 2 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(DEEP_W));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
     if (A_FIRST) {
-      if (STEADY || kt + NA < nk) issueA(a_slot(u % NA), kt + NA);
+      if (STEADY || kt + NA < nk) issueA(live_c, a_slot(u % NA), kt + NA);
       if (STEADY || kt + NB < nk) issueB(b_slot(u % NB), kt + NB);
     } else {
       if (STEADY || kt + NB < nk) issueB(b_slot(u % NB), kt + NB);
-      if (STEADY || kt + NA < nk) issueA(a_slot(u % NA), kt + NA);
+      if (STEADY || kt + NA < nk) issueA(live_c, a_slot(u % NA), kt + NA);
     }
   };
 
-  // MFMA row blocks dealt to the wave rows as evenly as possible (see above)
-  const int nb = (rows + MB - 1) / MB;
-  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
-  const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
   const int lr = lane % MB, lk = lane / MB;
   const int sw = swz<BK>(lr);
 
@@ -680,7 +693,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][m], fb[slot][n],
                                                               acc[m][n], 0, 0, 0);
     };
-    prologue();
+    prologue(live_c);
     load_frags(a_slot(0), b_slot(0), 0, 0);
     // one K step on the slots of step kt (u = kt % 6); the hand-over sits
     // before the last sub-step's MFMAs, which cover the next slots' first reads
@@ -693,7 +706,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
       for (int sub = 0; sub < C::KSUB; ++sub) {
         if (sub + 1 < C::KSUB) load_frags(ca, cb, sub + 1, (sub + 1) & 1);
         if (sub == C::KSUB - 1 && (STEADY || kt + 1 < nk)) {
-          handover(sc, kt, steady_c);
+          handover(live_c, sc, kt, steady_c);
           load_frags(a_slot((u + 1) % NA), b_slot((u + 1) % NB), 0, 0);
         }
         // keep the reads issued above ahead of this sub-step's MFMAs
@@ -717,14 +730,15 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     default: {
       // this wave row holds no valid row: make its copies and keep the
       // barrier count of the others
-      prologue();
+      const std::integral_constant<int, 0> none{};
+      prologue(none);
       int kt = 0;
       for (; kt + 6 < nk; kt += 6)
-        unroll<6>([&](auto uc) { handover(uc, kt + decltype(uc)::value, std::false_type{}); });
+        unroll<6>([&](auto uc) { handover(none, uc, kt + decltype(uc)::value, std::false_type{}); });
       for (; kt + 1 < nk; kt += 6)
         unroll<6>([&](auto uc) {
           if (kt + decltype(uc)::value + 1 < nk)
-            handover(uc, kt + decltype(uc)::value, std::false_type{});
+            handover(none, uc, kt + decltype(uc)::value, std::false_type{});
         });
     }
   }
