@@ -25,6 +25,7 @@ METRIC = "MoE-layer tokens/s @GLM-5.2 shape (T=64 decode, T=8192 prefill); % roo
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_CLOCK_MHZ = 2400.0     # engine clock of the published MFMA peaks
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gate_up_glm.json")
 KERNEL_SOURCES = ("gemm_bf16.hip", "common.h", "permute.hip", "glm_moe.hip")
 
@@ -106,6 +107,19 @@ def with_measured(roof, peaks=None):
     return roof
 
 
+def at_clock(roof, clock):
+    """MFMA-bound roofline: also the fraction of the peak scaled to the mean
+    shader clock measured over the calls (the published peak is at the
+    2400 MHz peak engine clock)."""
+    if roof["bound"] != "mfma" or not clock:
+        return roof
+    clk = clock["mean"]
+    roof["clock_mhz_timed"] = clk
+    roof["peak_at_clock"] = round(roof["peak"] * clk / PEAK_CLOCK_MHZ, 1)
+    roof["frac_at_clock"] = round(roof["achieved"] / roof["peak_at_clock"], 4)
+    return roof
+
+
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -137,6 +151,37 @@ def algorithmic(w, counts):
     return f, b, layer_flops, layer_bytes, n_active
 
 
+def probe_clock(torch, call, steps, seconds):
+    """Mean shader clock (MHz) over `steps` more calls: a one-wave probe
+    (libglm_peaks.so) on a side stream samples the shader clock counter
+    against the 100 MHz constant counter every 100 us for `seconds` (set a
+    little shorter than the calls) while they run."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_transformer_glm_amd", "libglm_peaks.so"))
+    L.glm_peak_clock_probe.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    n = 4096
+    buf = torch.zeros(2 * n + 1, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    st = L.glm_peak_clock_probe(min(max(seconds, 1e-3), 10.0), 100, n, buf.data_ptr(),
+                                side.cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"glm_peak_clock_probe failed: hipError {st}")
+    for _ in range(steps):
+        call(None)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy().astype("uint64")
+    m = int(b[2 * n])
+    if m < 3:
+        return None
+    c = b[0:2 * m:2].astype("float64")
+    r = b[1:2 * m:2].astype("float64")
+    mhz = 100.0 * (c[1:] - c[:-1]) / (r[1:] - r[:-1])
+    return {"mean": round(float(mhz.mean()), 0), "min": round(float(mhz.min()), 0),
+            "max": round(float(mhz.max()), 0), "samples": int(m - 1)}
+
+
 def time_calls(glm, torch, call, steps, warmup):
     """Run ``call(trace)`` warmup + steps times untraced; wall time of the
     timed steps (synchronised on both sides); then the same number of calls
@@ -150,6 +195,9 @@ def time_calls(glm, torch, call, steps, warmup):
         call(None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # then the shader clock over as many calls again (a separate pass, so the
+    # probe's wave does not take part in the timed one)
+    time_calls.clock = probe_clock(torch, call, steps, 0.9 * elapsed)
     tr = glm.Trace(max_calls=steps)
     for _ in range(steps):
         call(tr)
@@ -276,7 +324,7 @@ def dense_record(glm, torch, w, F, dw, steps, warmup, ws, bound):
                 "work_per_launch": b[dom], "avg_launch_ms": round(pc[dom], 4)}
     return {"workload": f"dense FFN hidden {D} width {F}, {T} tokens", "tokens": T,
             "value": round(T * steps / elapsed, 1), "unit": "tokens/s", "steps": steps,
-            "ms_per_step": round(ms, 4), "roofline": with_measured(roof),
+            "ms_per_step": round(ms, 4), "roofline": at_clock(with_measured(roof), time_calls.clock),
             "stages_ms": {s: round(v, 4) for s, v in pc.items() if v > 0}}
 
 
@@ -361,6 +409,7 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
         d = dev.with_x(to_device(wl.make_x(w)), to_device(wl.make_corr_bias(w)), w)
         e, pc, c = time_layer(glm, torch, d, w, args.steps, args.warmup, ws)
         ms, roof, layer, load = record(w, e, args.steps, pc, c, bound)
+        at_clock(roof, time_calls.clock)
         res[key] = {"workload": name, "tokens": w.T, "hot_bias": w.hot_value,
                     "value": round(w.T * args.steps / e, 1), "unit": "tokens/s",
                     "ms_per_step": round(ms, 4), "roofline": roof, "layer_roofline": layer,
@@ -380,6 +429,7 @@ def variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args):
         _, _, lf, lb, _ = algorithmic(w, c)
         bound = "mfma" if lf / (PEAK_BF16_TFLOPS * 1e12) > lb / (PEAK_HBM_GBS * 1e9) else "hbm"
         ms, roof, layer, load = record(w, e, args.steps, pc, c, bound)
+        at_clock(roof, time_calls.clock)
         sweep[str(T)] = {"value": round(T * args.steps / e, 1), "unit": "tokens/s",
                          "ms_per_step": round(ms, 4), "roofline": roof, "layer_roofline": layer,
                          "routing_load": load, "call_ms": pc["_pct"]}
@@ -423,6 +473,7 @@ def mx_records(glm, torch, wl, args):
                                            to_device(wl.make_corr_bias(w)), w)
         e, pc, c = time_layer(glm, torch, d, w, steps, args.warmup, ws)
         ms, roof, layer, load = record(w, e, steps, pc, c, bound)
+        at_clock(roof, time_calls.clock)
         res[key] = {"workload": w.name, "tokens": w.T, "value": round(w.T * steps / e, 1),
                     "unit": "tokens/s", "steps": steps, "ms_per_step": round(ms, 4),
                     "roofline": roof, "layer_roofline": layer, "routing_load": load,
@@ -486,8 +537,10 @@ def main():
     ws = torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
 
     elapsed, per_call, counts = time_layer(glm, torch, dev, wp, args.steps, args.warmup, ws)
+    gpu = time_calls.clock
     ms, roof, layer, load = record(wp, elapsed, args.steps, per_call, counts, "mfma",
                                    "prefill" if wp.name == "glm_prefill" else None)
+    at_clock(roof, gpu)
     value = wp.T * args.steps / elapsed
     log(f"prefill: {value:,.0f} tokens/s, {ms:.3f} ms/step, stages {stages(per_call)}")
     route_ms = time_route(glm, torch, dev, wp, args.steps, args.warmup, ws)
@@ -503,7 +556,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof, "layer_roofline": layer, "routing_load": load,
         "stages_ms": stages(per_call), "call_ms": per_call["_pct"], "route_ms": route_ms,
-        "measured_peaks": peaks,
+        "measured_peaks": peaks, "shader_clock_mhz": gpu,
     }
 
     if wd:
@@ -511,6 +564,7 @@ def main():
                        to_device(wl.make_corr_bias(wd)), dev.w1, dev.w3, dev.w2, dev.sw1,
                        dev.sw3, dev.sw2)
         e2, pc2, c2 = time_layer(glm, torch, dd, wd, args.decode_steps, args.warmup, ws)
+        gpu2 = time_calls.clock
         ms2, roof2, layer2, load2 = record(wd, e2, args.decode_steps, pc2, c2, "hbm",
                                            "decode" if wd.name == "glm_decode" else None)
         v2 = wd.T * args.decode_steps / e2
@@ -521,7 +575,7 @@ def main():
                           "ms_per_step": round(ms2, 4), "roofline": roof2,
                           "layer_roofline": layer2, "routing_load": load2,
                           "stages_ms": stages(pc2), "call_ms": pc2["_pct"],
-                          "route_ms": route2}
+                          "route_ms": route2, "shader_clock_mhz": gpu2}
 
     if args.variants:
         line["variants"] = variants(glm, torch, wl, dev, wp, wd, ws, norm_w, args)

@@ -34,11 +34,24 @@ int glm_peak_mfma(int fp8, int iters, int blocks_per_cu, void* scratch, float* m
 
 /* Streaming HBM read bandwidth.  Reads `bytes` (a multiple of 16) from the
  * device buffer `src` (16-byte aligned; make it far larger than the 256 MB
- * last-level cache) with 16-byte non-temporal loads, once untimed and then
- * `reps` timed times; *ms (host pointer) receives the fastest launch.
+ * last-level cache) with 16-byte non-temporal loads, in two launch shapes
+ * (32 workgroups of 256 threads per compute unit with 8 loads in flight per
+ * thread; 64 with 4), each once untimed and then `reps` timed times; *ms
+ * (host pointer) receives the fastest launch.
  * `scratch`: caller-owned device buffer of at least 2048 * 256 * 4 bytes. */
 int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, float* ms,
                       hipStream_t stream);
+
+/* Shader clock while other work runs.  Launches one wave on `stream` (do not
+ * wait for it) that, every `period_us` microseconds for `seconds` (0 < seconds
+ * <= 10) or until `max_samples` samples, stores the pair (shader clock
+ * counter, 100 MHz constant counter) to buf[2i], buf[2i+1], then the number
+ * of pairs to buf[2 * max_samples].  Clock in MHz between two samples:
+ * 100 * (difference of the first words) / (difference of the second).
+ * `buf`: caller-owned device buffer of 2 * max_samples + 1 uint64 words,
+ * valid once the stream has passed the probe.  Returns without waiting. */
+int glm_peak_clock_probe(double seconds, int period_us, int max_samples, void* buf,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,8 +9,8 @@
 //  * fp8 MFMA: the same loop on the block-scaled v_mfma_scale_f32_32x32x64_f8f6f4
 //    (E4M3 operands, unit scales), the instruction of the MXFP8 layer.
 //  * HBM read: a streaming read of a buffer far larger than the last-level
-//    cache (16-byte non-temporal loads, one sum per thread so the loads are
-//    not removed), the way the grouped GEMMs stream expert weights.
+//    cache (16-byte non-temporal loads, many workgroups per CU so enough
+//    requests are in flight; the fastest of two launch shapes).
 //
 // Separate library (libglm_peaks.so): measurement only, not part of the layer.
 #include <hip/hip_runtime.h>
@@ -30,6 +30,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChains = 8;  // independent accumulators per wave
+constexpr int kSinkWords = 2048 * 256;  // words of the read kernel's sink (scratch)
 
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float seed, float* sink,
                                                         unsigned long long* clocks) {
@@ -96,24 +97,54 @@ __global__ __launch_bounds__(256) void mfma_fp8_loop_kernel(int iters, int seed,
   }
 }
 
+// U independent 16-byte loads in flight per thread and loop trip.
+template <int U>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src,
                                                           size_t n16, uint32_t* sink) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   uint32_t acc = 0;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 v0 = __builtin_nontemporal_load(src + i);
-    const u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w ^ v2.x ^ v2.y ^ v2.z ^ v2.w ^
-           v3.x ^ v3.y ^ v3.z ^ v3.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
     const u32x4 v = __builtin_nontemporal_load(src + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
-  if (acc == 0x9E3779B9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;  // keeps the loads
+  // keeps the loads; never true for the buffers read here
+  if (acc == 0x9E3779B9u) sink[(blockIdx.x * blockDim.x + threadIdx.x) % kSinkWords] = acc;
+}
+
+// One wave: every `period` ticks of the 100 MHz constant counter, lane 0
+// stores (shader clock counter, constant counter) to out[2i], out[2i+1];
+// stops after `ticks` or `max_samples` samples and stores the count at
+// out[2 * max_samples].
+__global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long ticks,
+                                                         unsigned long long period,
+                                                         int max_samples,
+                                                         unsigned long long* out) {
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long next = r0;
+  int n = 0;
+  while (n < max_samples) {
+    const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+    if (r - r0 > ticks) break;
+    if (r >= next) {
+      const unsigned long long c = __builtin_amdgcn_s_memtime();
+      if (threadIdx.x == 0) {
+        out[2 * n] = c;
+        out[2 * n + 1] = r;
+      }
+      ++n;
+      next += period;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+  if (threadIdx.x == 0) out[2 * max_samples] = (unsigned long long)n;
 }
 
 int num_cus() {
@@ -166,31 +197,56 @@ GLM_PEAKS_API int glm_peak_mfma(int fp8, int iters, int blocks_per_cu, void* scr
 
 // Streaming read of `bytes` (a multiple of 16) from `src` (device memory, at
 // least 16-byte aligned), timed with HIP events: writes the best of `reps`
-// launches in ms.  `scratch` holds at least 2048 * 256 * 4 bytes.
+// launches of each of two launch shapes (32 workgroups per CU with 8 loads in
+// flight per thread, 64 with 4) in ms.  `scratch` holds at least
+// 2048 * 256 * 4 bytes.
 GLM_PEAKS_API int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch,
                                     float* ms, hipStream_t stream) {
   const int cus = num_cus();
   if (cus <= 0 || !src || !scratch || !ms || bytes % 16 || reps <= 0) return hipErrorInvalidValue;
-  const int blocks = cus * 8 > 2048 ? 2048 : cus * 8;
   hipEvent_t e0, e1;
   hipError_t r;
   if ((r = hipEventCreate(&e0)) != hipSuccess) return r;
   if ((r = hipEventCreate(&e1)) != hipSuccess) return r;
   const u32x4* p = static_cast<const u32x4*>(src);
   uint32_t* sink = static_cast<uint32_t*>(scratch);
-  stream_read_kernel<<<blocks, 256, 0, stream>>>(p, bytes / 16, sink);  // warm-up
+  const size_t n16 = bytes / 16;
+  auto launch = [&](int shape) {
+    if (shape == 0) stream_read_kernel<8><<<cus * 32, 256, 0, stream>>>(p, n16, sink);
+    else stream_read_kernel<4><<<cus * 64, 256, 0, stream>>>(p, n16, sink);
+  };
   float best = 1e30f;
-  for (int i = 0; i < reps && r == hipSuccess; ++i) {
-    (void)hipEventRecord(e0, stream);
-    stream_read_kernel<<<blocks, 256, 0, stream>>>(p, bytes / 16, sink);
-    (void)hipEventRecord(e1, stream);
-    float t = 0.f;
-    if ((r = hipEventSynchronize(e1)) == hipSuccess) r = hipEventElapsedTime(&t, e0, e1);
-    if (r == hipSuccess && t < best) best = t;
+  for (int shape = 0; shape < 2 && r == hipSuccess; ++shape) {
+    launch(shape);  // warm-up
+    for (int i = 0; i < reps && r == hipSuccess; ++i) {
+      (void)hipEventRecord(e0, stream);
+      launch(shape);
+      (void)hipEventRecord(e1, stream);
+      float t = 0.f;
+      if ((r = hipEventSynchronize(e1)) == hipSuccess) r = hipEventElapsedTime(&t, e0, e1);
+      if (r == hipSuccess && t < best) best = t;
+    }
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (r != hipSuccess) return r;
   *ms = best;
   return hipSuccess;
+}
+
+// Shader clock while other work runs: launches one wave on `stream` that
+// samples the shader clock counter against the 100 MHz constant counter every
+// `period_us` microseconds for `seconds` (at most 10) or `max_samples`
+// samples, and returns without waiting.  `buf`: caller-owned device buffer of
+// 2 * max_samples + 1 unsigned 64-bit words (pairs, then the count), valid
+// once the stream has passed the probe.  A SIMD holding the probe wave may
+// not fit a workgroup that needs its whole register file.
+GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_samples, void* buf,
+                                       hipStream_t stream) {
+  if (!(seconds > 0.0) || seconds > 10.0 || period_us <= 0 || max_samples <= 0 || !buf)
+    return hipErrorInvalidValue;
+  const unsigned long long ticks = (unsigned long long)(seconds * 1e8);
+  clock_probe_kernel<<<1, 64, 0, stream>>>(ticks, (unsigned long long)period_us * 100,
+                                           max_samples, static_cast<unsigned long long*>(buf));
+  return hipGetLastError();
 }
