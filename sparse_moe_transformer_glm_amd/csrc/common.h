@@ -44,6 +44,9 @@ constexpr int kXcdBlockMxGu = GLM_XCD_BLOCK_MX_GU, kXcdBlockMxDn = GLM_XCD_BLOCK
 #define GLM_XCD_BLOCK_DECODE_DN 128
 #endif
 constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
+#ifndef GLM_XCD_BLOCK_FEW  // the dense layer's few decode tiles (both GEMMs)
+#define GLM_XCD_BLOCK_FEW 1
+#endif
 // Average rows per expert up to which the two-stage gate/up and down GEMMs
 // issue each refill before their wait (GateUpArgs::early, DownArgs::early).
 // Measured: the two orders are equal at 160 rows per expert, the plain order
@@ -63,8 +66,10 @@ constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
 #endif
 constexpr int32_t kSoleRowTile = 1 << 16;  // TileDesc::group flag
 constexpr int32_t kGroupMask = kSoleRowTile - 1;
-// TileDesc::group bits 20 and up: K chunk of a down tile of the shared (dense)
-// group when its contraction is split (DownArgs::ksplit > 1)
+constexpr int32_t kChunkTile = 1 << 17;  // TileDesc::group flag: a gate/up K chunk
+// TileDesc::group bits 20 and up: K chunk of a tile of the shared (dense)
+// group when its contraction is split (DownArgs::ksplit > 1; gate/up tiles
+// flagged kChunkTile)
 constexpr int kKChunkShift = 20;
 constexpr int kCpolNt = 2;  // cache-policy immediate of the LDS-DMA load: NT
 template <int BM, int BN>
@@ -125,6 +130,10 @@ struct ScanParams {
   GemmShape gu, dn;
   int gu_desc_cap, dn_desc_cap;
   int dn_ksplit;               // K chunks of the shared group's down tiles (1: whole K)
+  // the shared group's gate/up tiles: the first gu_whole in column-tile-major
+  // order run whole, the others in gu_ksplit K chunks each; gu_shared_n is
+  // the number of descriptors (whole tiles plus chunks)
+  int gu_ksplit, gu_whole, gu_shared_n;
 };
 hipError_t launch_scan(const uint64_t* masks, const ScanParams& p,
                        int32_t* counts, int32_t* offsets, int32_t* tile_base,
@@ -153,13 +162,29 @@ struct GateUpArgs {
   int grid;                    // launched workgroups (>= desc_count, multiple of 8)
   int xblk;                    // XCD block of the tile mapping (xcd_tile)
   int early;                   // two-stage tiles: issue each refill before the wait
+  // K chunks of the shared group's tiles flagged kChunkTile (a dense layer on
+  // a decode-size batch only): chunk kc of such a tile writes its fp32 sums
+  // for hidden column pc0 + c, gate to P[kc][t][c] and up to P[kc][t][pw + c],
+  // and launch_gateup_fixup forms those columns of Hs
+  int ksplit;
+  float* P;
+  int pc0, pw;
 };
 // Tile shape of a grouped GEMM launch.  `wide` says the output width allows
 // the 256-column tiles (gate/up: F and F_shared multiples of 128; down and
 // shared-combine: D a multiple of 256); otherwise 64-column tiles are used.
 GemmShape gemm_shape(double rows_per_group, bool wide);
+// Tile shape for a single group of `rows` (at most 96) rows: the dense layer
+// on a decode-size batch.
+GemmShape gemm_shape_few(int rows, bool wide);
+// Workgroups of a bf16 tile shape's kernel that fit on one CU at once.
+int gemm_wgs_per_cu(GemmShape sh);
 
 hipError_t launch_gateup_bf16(const GateUpArgs& a, GemmShape sh, hipStream_t s);
+// Hs[t][c0 + c] = bf16(SiLU(sum_kc P[kc][t][c]) * sum_kc P[kc][t][w + c]) for
+// c < w, chunks summed in order (c0 and w multiples of 4).
+hipError_t launch_gateup_fixup(const float* P, bf16_t* Hs, int T, int Fs, int c0, int w, int ks,
+                               hipStream_t s);
 
 struct DownArgs {
   const bf16_t* H;             // [T*k][F]

@@ -140,6 +140,26 @@ __device__ __forceinline__ void tile_epilogue(const GateUpArgs& gu, const DownAr
     bf16_t* Hb = (shared ? gu.Hs : gu.H) + (size_t)row0 * F;
     constexpr int HC = TN / 2;  // hidden columns of this wave
     __syncthreads();            // every wave is done reading the stages
+    if (kc >= 0) {  // a K chunk: its fp32 sums of gate and up
+      float* Pk = gu.P + ((size_t)kc * gu.T + row0) * (2 * gu.pw);
+#pragma unroll
+      for (int m = 0; m < FM; ++m) {
+        if (m >= live_m) continue;
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q) {
+          const int hcol = col0 + (wn * TN / (2 * MB) + q) * MB + lr - gu.pc0;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const int row = row_of(m, r);
+            if (row < rows) {
+              store_stream(Pk + (size_t)row * (2 * gu.pw) + hcol, acc[m][2 * q][r]);
+              store_stream(Pk + (size_t)row * (2 * gu.pw) + gu.pw + hcol, acc[m][2 * q + 1][r]);
+            }
+          }
+        }
+      }
+      return;
+    }
     if constexpr (GU_LDS) {
       // Through LDS, one MB-row block at a time (as the down epilogue):
       // 16-byte stores of 8 consecutive hidden values.
@@ -273,6 +293,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     const TileDesc d = gu.desc[i];
     g = d.group & kGroupMask; sole = d.group & kSoleRowTile; row0 = d.row0; rows = d.rows;
     col0 = d.col0; K = gu.D;
+    kc = -1;
+    if (d.group & kChunkTile) {  // one K chunk of a shared-group tile
+      kc = d.group >> kKChunkShift;
+      K = gu.D / gu.ksplit;
+      koff = kc * K;
+    }
   } else {
     const int i = xcd_tile(*dn.desc_count, dn.xblk);
     if (i < 0) return;
@@ -539,6 +565,12 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     if (i < 0) return;
     const TileDesc d = gu.desc[i];
     g = d.group & kGroupMask; row0 = d.row0; rows = d.rows; col0 = d.col0; K = gu.D;
+    kc = -1;
+    if (d.group & kChunkTile) {  // one K chunk of a shared-group tile
+      kc = d.group >> kKChunkShift;
+      K = gu.D / gu.ksplit;
+      koff = kc * K;
+    }
   } else {
     const int i = xcd_tile(*dn.desc_count, dn.xblk);
     if (i < 0) return;
@@ -808,6 +840,12 @@ using CfgMid = Cfg<GLM_CFG_MID>;
 #endif
 using CfgBig = Cfg<GLM_CFG_BIG>;  // prefill: 8 waves (two per SIMD), BK 64, 2 stages
 using CfgNarrow = Cfg<32, 64, 64, 1, 2, 4, 16>;    // widths that are not a multiple of 128/256
+// a dense layer on 33..96 tokens: one row tile up to 64 tokens, so each
+// weight slice is streamed by one workgroup
+#ifndef GLM_CFG_DECODE64
+#define GLM_CFG_DECODE64 64, 128, 64, 1, 4, 5, 16
+#endif
+using CfgDecode64 = Cfg<GLM_CFG_DECODE64>;
 
 #ifndef GLM_SPLIT_BIG
 #define GLM_SPLIT_BIG 1
@@ -841,6 +879,8 @@ hipError_t dispatch(GemmShape sh, const GateUpArgs& gu, const DownArgs& dn, unsi
   if (sh.BM == CfgBig::BM && sh.BN == CfgBig::BN) return launch_one<CfgBig, MODE>(gu, dn, grid, s);
   if (sh.BM == CfgNarrow::BM && sh.BN == CfgNarrow::BN)
     return launch_one<CfgNarrow, MODE>(gu, dn, grid, s);
+  if (sh.BM == CfgDecode64::BM && sh.BN == CfgDecode64::BN)
+    return launch_one<CfgDecode64, MODE>(gu, dn, grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -858,12 +898,62 @@ GemmShape gemm_shape(double rows_per_group, bool wide) {
   return {CfgBig::BM, CfgBig::BN};
 }
 
+// Workgroups of the config with tile shape `sh` that fit on one CU at once
+// (LDS: the stage ring; 160 KB per CU).
+template <class C>
+constexpr int wgs_per_cu() {
+  return (160 * 1024) / (C::ST * C::STAGE * 2 + C::BM * 8);
+}
+int gemm_wgs_per_cu(GemmShape sh) {
+  if (sh.BM == CfgDecode::BM && sh.BN == CfgDecode::BN) return wgs_per_cu<CfgDecode>();
+  if (sh.BM == CfgDecode64::BM && sh.BN == CfgDecode64::BN) return wgs_per_cu<CfgDecode64>();
+  if (sh.BM == CfgNarrow::BM && sh.BN == CfgNarrow::BN) return wgs_per_cu<CfgNarrow>();
+  if (sh.BM == CfgMid::BM && sh.BN == CfgMid::BN) return wgs_per_cu<CfgMid>();
+  return 1;
+}
+
+GemmShape gemm_shape_few(int rows, bool wide) {
+  if (!wide) return {CfgNarrow::BM, CfgNarrow::BN};
+  if (rows <= CfgDecode::BM) return {CfgDecode::BM, CfgDecode::BN};
+  return {CfgDecode64::BM, CfgDecode64::BN};
+}
+
 hipError_t launch_gateup_bf16(const GateUpArgs& a, GemmShape sh, hipStream_t s) {
   return dispatch<GATE_UP>(sh, a, DownArgs{}, (unsigned)a.grid, s);
 }
 
 hipError_t launch_down_bf16(const DownArgs& a, GemmShape sh, hipStream_t s) {
   return dispatch<DOWN>(sh, GateUpArgs{}, a, (unsigned)a.grid, s);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void gateup_fixup_kernel(const float* __restrict__ P,
+                                                           bf16_t* __restrict__ Hs, int T, int Fs,
+                                                           int c0, int w, int ks) {
+  const int W4 = w / 4;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * W4) return;
+  const int t = (int)(i / W4), c = (int)(i % W4) * 4;
+  f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < ks; ++kc) {
+    const float* p = P + ((size_t)kc * T + t) * (2 * w);
+    g += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + c));
+    u += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + w + c));
+  }
+  bf16_t h[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = f32_to_bf16(silu(g[j]) * u[j]);
+  *reinterpret_cast<uint2*>(Hs + (size_t)t * Fs + c0 + c) =
+      make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+}
+}  // namespace
+
+hipError_t launch_gateup_fixup(const float* P, bf16_t* Hs, int T, int Fs, int c0, int w, int ks,
+                               hipStream_t s) {
+  const size_t n = (size_t)T * (w / 4);
+  if (n == 0) return hipSuccess;
+  gateup_fixup_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(P, Hs, T, Fs, c0, w, ks);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* Y, float* out, int T, int D, int k, const void* residual,

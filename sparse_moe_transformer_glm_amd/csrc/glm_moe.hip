@@ -40,14 +40,63 @@ struct Plan {
   GemmShape gu, dn;
   int gu_cap, dn_cap;
   int dn_ksplit;     // K chunks of the shared (dense) group's down tiles
+  int gu_ksplit;     // K chunks of its gate/up tiles past the first gu_whole
+  int gu_whole, gu_shared_n;  // (see ScanParams)
+  int gu_pc0, gu_pw;          // hidden columns [pc0, pc0 + pw) come from K chunks
+  bool few_tiles;             // dense layer on a decode-size batch
   GroupRouting gr;
   const float* norm_weight;
   float norm_eps;
   bool add_residual;
   size_t xnorm, partial, idx, w, masks, tile_base, counts, offsets, gu_count, dn_count, gu_desc,
-      dn_desc, row_assign, row_w, H, Hs, Y, xq, xs, xsp, Hsc, Hssc;
+      dn_desc, row_assign, row_w, H, Hs, Y, Pgu, xq, xs, xsp, Hsc, Hssc;
   size_t total;
 };
+
+// K chunks for the few tiles of a dense layer on a decode-size batch: the
+// divisor ks of the K steps, in chunks of at least 16 steps, that minimises
+// the rounds of tiles * ks over the 256 CUs (`per_cu` workgroups each) times
+// (steps per chunk + 4), the last term a tile's fixed cost (pipeline fill,
+// epilogue) counted in K steps.
+int ksplit_for(int tiles, int ksteps, int per_cu) {
+  const int slots = 256 * (per_cu > 0 ? per_cu : 1);
+  int best = 1;
+  long long best_t = -1;
+  for (int ks = 1; ks == 1 || ks <= ksteps / 16; ++ks) {
+    if (ksteps % ks) continue;
+    const long long t = (long long)cdiv(tiles * ks, slots) * (ksteps / ks + 4);
+    if (best_t < 0 || t < best_t) { best_t = t; best = ks; }
+  }
+  return best;
+}
+
+// Gate/up K split of the dense layer on a decode-size batch.  With `slots`
+// = 256 CUs x `per_cu` workgroups, the first whole * slots tiles (column-tile
+// major, `mt` row tiles per column) run whole, and the rest, rounded up to
+// whole columns of tiles, run in *ks K chunks so that every slot gets one
+// chunk: ks the largest divisor of the K steps with rest * ks <= slots and
+// chunks of at least 8 steps.  Every CU then streams about the same number
+// of K steps.  With fewer tiles than slots all run in chunks (ksplit_for).
+void plan_gateup_split(int tiles, int mt, int ksteps, int per_cu, int* whole, int* ks) {
+  const int slots = 256 * (per_cu > 0 ? per_cu : 1);
+  *whole = tiles;
+  *ks = 1;
+  if (tiles <= 0 || mt <= 0) return;
+  if (tiles < slots) {
+    *ks = ksplit_for(tiles, ksteps, per_cu);
+    *whole = *ks > 1 ? 0 : tiles;
+    return;
+  }
+  int rest = tiles % slots;
+  rest = cdiv(rest, mt) * mt;
+  if (rest == 0) return;
+  int best = 1;
+  for (int c = 2; c * 8 <= ksteps; ++c)
+    if (ksteps % c == 0 && (long long)rest * c <= slots) best = c;
+  if (best < 2) return;
+  *whole = tiles - rest;
+  *ks = best;
+}
 
 int desc_cap(int A, int E, GemmShape s, int ncol_tiles) {
   const long nz = A < E ? A : E;
@@ -148,32 +197,42 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
     const bool wide_gu = (dense || P.F % 128 == 0) && P.Fs % 128 == 0;
     const bool wide_dn = P.D % 256 == 0;
     // A dense layer on a decode-size batch is a single group of a few rows:
-    // its weights are streamed on the decode tiles (32 x 128), and the down
-    // projection, whose few column tiles would leave most CUs idle (96 tiles
-    // at 64 tokens and hidden 6144), splits its contraction into K chunks
-    // that write separate slots of Y, summed in order by the combine.
+    // its weights are streamed on the decode tiles (32 or 64 x 128, one row
+    // tile up to 64 tokens), and both GEMMs, whose few column tiles would
+    // leave CUs idle or fill them unevenly (288 gate/up and 48 down tiles at
+    // 64 tokens, hidden 6144, width 18432), split their contraction into K
+    // chunks: down chunks write separate slots of Y, summed in order by the
+    // combine; gate/up chunks write fp32 sums that a fixup kernel adds in
+    // order before the SiLU product.
     const bool few_tiles = dense && per_group <= 96.0;
-    P.gu = mx ? gemm_shape_mx(per_group, wide_gu) : gemm_shape(few_tiles ? 1.0 : per_group, wide_gu);
-    P.dn = mx ? gemm_shape_mx(per_group, wide_dn) : gemm_shape(few_tiles ? 1.0 : per_group, wide_dn);
-    P.dn_ksplit = 1;
+    P.few_tiles = few_tiles;
+    P.gu = mx ? gemm_shape_mx(per_group, wide_gu)
+              : few_tiles ? gemm_shape_few(T, wide_gu) : gemm_shape(per_group, wide_gu);
+    P.dn = mx ? gemm_shape_mx(per_group, wide_dn)
+              : few_tiles ? gemm_shape_few(T, wide_dn) : gemm_shape(per_group, wide_dn);
+    P.dn_ksplit = P.gu_ksplit = 1;
+    const int gu_mt = cdiv(T, P.gu.BM), gu_tiles = gu_mt * (2 * P.Fs / P.gu.BN);
+    P.gu_whole = gu_tiles;
     if (few_tiles && T > 0) {
-      const int tiles = cdiv(T, P.dn.BM) * (P.D / P.dn.BN);
-      const int ksteps = P.Fs / 64;
-      int ks = cdiv(512, tiles);
-      if (ks > ksteps / 16) ks = ksteps / 16;  // chunks of at least 16 K steps
-      while (ks > 1 && ksteps % ks) --ks;      // whole K steps per chunk
-      P.dn_ksplit = ks < 1 ? 1 : ks;
+      plan_gateup_split(gu_tiles, gu_mt, P.D / 64, gemm_wgs_per_cu(P.gu), &P.gu_whole,
+                        &P.gu_ksplit);
+      P.dn_ksplit = ksplit_for(cdiv(T, P.dn.BM) * (P.D / P.dn.BN), P.Fs / 64,
+                               gemm_wgs_per_cu(P.dn));
     }
+    P.gu_shared_n = P.gu_whole + (gu_tiles - P.gu_whole) * P.gu_ksplit;
+    P.gu_pc0 = (P.gu_whole / (gu_mt > 0 ? gu_mt : 1)) * (P.gu.BN / 2);
+    P.gu_pw = P.gu_ksplit > 1 ? P.Fs - P.gu_pc0 : 0;
     // tile-list capacity: routed tiles plus the shared (or dense) group's (group E)
-    P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) +
-               cdiv(T, P.gu.BM) * (2 * P.Fs / P.gu.BN);
+    P.gu_cap = (dense ? 0 : desc_cap(A, P.E, P.gu, 2 * P.F / P.gu.BN)) + P.gu_shared_n;
     P.dn_cap = (dense ? 0 : desc_cap(A, P.E, P.dn, P.D / P.dn.BN)) +
                cdiv(T, P.dn.BM) * (P.D / P.dn.BN) * P.dn_ksplit;
   } else {
     P.ksplit = 1; P.kchunk = P.D;
     P.gu = P.dn = GemmShape{0, 0};
     P.gu_cap = P.dn_cap = 0;
-    P.dn_ksplit = 1;
+    P.few_tiles = false;
+    P.dn_ksplit = P.gu_ksplit = 1;
+    P.gu_whole = P.gu_shared_n = P.gu_pc0 = P.gu_pw = 0;
   }
 
   const size_t act = bf16 ? 2 : 4;
@@ -198,6 +257,8 @@ int make_plan(const glm_moe_dims* d, int top_k, const glm_moe_options* opts, boo
   P.Hs = take((size_t)T * P.Fs * hid);
   // [T][k+ks][D]: slots k .. k+ks-1 hold the shared expert (ks K chunks)
   P.Y = take((size_t)T * (P.k + P.dn_ksplit) * P.D * 4);
+  // gate and up sums of the shared group's K chunks (gate/up K split only)
+  P.Pgu = take(P.gu_ksplit > 1 ? (size_t)P.gu_ksplit * T * 2 * P.gu_pw * 4 : 0);
   P.xq = take(mx ? (size_t)T * P.D : 0);        // MXFP8 input codes and scales
   P.xs = take(mx ? (size_t)T * P.D / 32 : 0);
   P.xsp = take(mx ? (size_t)A * P.D / 32 : 0);  // input scales in expert-row order
@@ -322,6 +383,9 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   sp.gu_desc_cap = P.gu_cap;
   sp.dn_desc_cap = P.dn_cap;
   sp.dn_ksplit = P.dn_ksplit;
+  sp.gu_ksplit = P.gu_ksplit;
+  sp.gu_whole = P.gu_whole;
+  sp.gu_shared_n = P.gu_shared_n;
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCAN));
   GLM_HIP(launch_scan(masks, sp, counts, offsets, tile_base, gu_desc, gu_count, dn_desc, dn_count, s));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));
@@ -372,13 +436,22 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     ga.desc = gu_desc; ga.desc_count = gu_count;
     ga.H = at<bf16_t>(ws, P.H); ga.Hs = at<bf16_t>(ws, P.Hs);
     ga.T = P.T; ga.D = P.D; ga.E = P.E; ga.F = P.F; ga.Fs = P.Fs; ga.k = P.k;
-    ga.xblk = (!P.dense && P.gu.BM == 256) ? kXcdBlockRoutedGu : kXcdBlock;
+    // (few tiles of a dense layer: listed round-robin over the XCDs, so every
+    // XCD gets the same share of whole tiles and K chunks)
+    ga.xblk = P.few_tiles ? GLM_XCD_BLOCK_FEW
+              : (!P.dense && P.gu.BM == 256) ? kXcdBlockRoutedGu : kXcdBlock;
     // Copy ahead of the wait on moderately filled 256-row tiles; at higher
     // average fill the second stage in flight congests the L2 miss path.
     ga.early = !P.dense && (double)P.T * P.k <= GLM_EARLY_MAX_ROWS * P.E;
+    ga.ksplit = P.gu_ksplit;
+    ga.P = at<float>(ws, P.Pgu);
+    ga.pc0 = P.gu_pc0;
+    ga.pw = P.gu_pw;
     ga.grid = xcd_grid(P.gu_cap, ga.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_GATE_UP));
     GLM_HIP(launch_gateup_bf16(ga, P.gu, s));
+    if (P.gu_ksplit > 1)
+      GLM_HIP(launch_gateup_fixup(ga.P, ga.Hs, P.T, P.Fs, P.gu_pc0, P.gu_pw, P.gu_ksplit, s));
 
     DownArgs da{};
     da.H = ga.H; da.Hs = ga.Hs; da.row_assign = row_assign;
@@ -386,7 +459,7 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
     da.row_w = row_w; da.desc = dn_desc; da.desc_count = dn_count; da.Y = Y;
     da.T = P.T; da.D = P.D; da.E = P.E; da.F = P.F; da.Fs = P.Fs; da.k = P.k;
     da.ksplit = P.dn_ksplit;
-    da.xblk = P.dn.BM == 32 ? kXcdBlockDecodeDn : kXcdBlock;
+    da.xblk = P.few_tiles ? GLM_XCD_BLOCK_FEW : P.dn.BM == 32 ? kXcdBlockDecodeDn : kXcdBlock;
     da.early = ga.early;  // same two-stage ring, same fill rule
     da.grid = xcd_grid(P.dn_cap, da.xblk);
     GLM_HIP(rec.mark(GLM_MOE_STAGE_DOWN));

@@ -58,7 +58,8 @@ __device__ inline int tile_row0(int m, int mt, int rows, int gran) {
 // previous round's last position, a few LDS reads per round.
 __device__ inline void write_descs(const int* pos, const int* og, int total, const int* cnt,
                                    const int* off, int T, int E, int BM, int shared_nt,
-                                   int col_w, int ksplit, TileDesc* __restrict__ out) {
+                                   int col_w, int ksplit, int whole,
+                                   TileDesc* __restrict__ out) {
   constexpr int kWaves = kScanThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int chunk = cdiv(cdiv(total, kWaves), kWave) * kWave;
@@ -78,24 +79,38 @@ __device__ inline void write_descs(const int* pos, const int* og, int total, con
     const int g = og[l];
     const int rows = g < E ? cnt[g] : T;
     const int mt = cdiv(rows, BM);
-    int nt, m, r0, rt, kc = 0;
+    int nt, m, r0, rt, kc = 0, chunk = 0;
     if (mt == 1 && g < E) {  // one row tile (the common case): no divisions
       m = 0;
       nt = i - pos[l];
       r0 = 0;
       rt = rows;
     } else {
-      // the shared group's K chunks count as extra column tiles (chunk innermost)
-      const int ks = g == E ? ksplit : 1;
-      tile_order(i - pos[l], mt, shared_nt * ks, g == E, &m, &nt);
+      if (g == E && whole >= 0) {
+        // gate/up of the shared group: `whole` tiles, then the others in
+        // `ksplit` K chunks (chunk innermost), tiles column-tile major
+        const int li = i - pos[l];
+        int t = li;
+        if (li >= whole) {
+          t = whole + (li - whole) / ksplit;
+          kc = (li - whole) % ksplit;
+          chunk = kChunkTile;
+        }
+        nt = t / mt;
+        m = t % mt;
+      } else {
+        // the shared group's K chunks count as extra column tiles (chunk innermost)
+        const int ks = g == E ? ksplit : 1;
+        tile_order(i - pos[l], mt, shared_nt * ks, g == E, &m, &nt);
+        kc = nt % ks;
+        nt /= ks;
+      }
       const int gran = min(64, BM);
       r0 = tile_row0(m, mt, rows, gran);
       rt = tile_row0(m + 1, mt, rows, gran) - r0;
-      kc = nt % ks;
-      nt /= ks;
     }
     TileDesc d;
-    d.group = g | (mt == 1 ? kSoleRowTile : 0) | (kc << kKChunkShift);
+    d.group = g | (mt == 1 ? kSoleRowTile : 0) | chunk | (kc << kKChunkShift);
     d.row0 = (g < E ? off[g] : 0) + r0;
     d.rows = rt;
     d.col0 = nt * col_w;
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
       s_dn[E] = dsum;
     }
     // the shared expert is group E of both GEMMs, over every token
-    s_gu[E + 1] = min(s_gu[E] + cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN), p.gu_desc_cap);
+    s_gu[E + 1] = min(s_gu[E] + p.gu_shared_n, p.gu_desc_cap);
     s_dn[E + 1] = min(s_dn[E] + cdiv(p.T, p.dn.BM) * (p.D / p.dn.BN) * p.dn_ksplit,
                       p.dn_desc_cap);
   }
@@ -260,7 +275,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     if (lpt_g) {
       const int rg = s_rank[0][tid];
       s_og[1 + rg] = tid;  // after the shared group's tiles:
-      s_pg[1 + rg] = cdiv(p.T, p.gu.BM) * (2 * p.Fs / p.gu.BN) + s_rank[1][tid];
+      s_pg[1 + rg] = p.gu_shared_n + s_rank[1][tid];
     } else {
       s_og[tid] = tid;
       s_pg[tid] = s_gu[tid];
@@ -284,9 +299,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
   // tile descriptors: groups in listing order, then output-column tile, then row tile
   write_descs(s_pg, s_og, s_gu[E + 1], s_cnt, s_off, p.T, E, p.gu.BM, 2 * p.Fs / p.gu.BN,
-              p.gu.BN / 2, 1, gu_desc);
+              p.gu.BN / 2, p.gu_ksplit, p.gu_ksplit > 1 ? p.gu_whole : -1, gu_desc);
   write_descs(s_pd, s_od, s_dn[E + 1], s_cnt, s_off, p.T, E, p.dn.BM, p.D / p.dn.BN, p.dn.BN,
-              p.dn_ksplit, dn_desc);
+              p.dn_ksplit, -1, dn_desc);
 }
 
 // One wave per 64-token tile.  A token's rank among the tile's tokens of
