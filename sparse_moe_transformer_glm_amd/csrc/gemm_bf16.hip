@@ -808,7 +808,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       v.x += u[j].x; v.y += u[j].y; v.z += u[j].z; v.w += u[j].w;
     }
   } else {
-    for (int j = 0; j < k; ++j) {
+    // four slots' loads in flight at a time; the adds stay in slot order
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      f32x4 u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[q] = __builtin_nontemporal_load(y + (size_t)(j + q) * D4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v.x += u[q].x; v.y += u[q].y; v.z += u[q].z; v.w += u[q].w;
+      }
+    }
+    for (; j < k; ++j) {
       const f32x4 u = __builtin_nontemporal_load(y + (size_t)j * D4);
       v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
     }
