@@ -306,6 +306,37 @@ def test_dense_zero_tokens():
     assert out.shape == (0, w.D)
 
 
+# Dense layers on decode-size batches split their few tiles over K: gate/up
+# runs whole tiles until every CU has one and the remaining column tiles in K
+# chunks (fixup kernel adds the chunks), or every tile in chunks when there
+# are fewer tiles than CUs; down splits every tile.  Each case takes another
+# branch of that plan: (T, D, dense width).
+DENSE_SPLIT_CASES = {
+    "rows32_whole_and_chunks": (16, 6144, 18432),   # 32-row tiles, 256 whole + 32 x 8 chunks
+    "rows64_two_row_tiles": (96, 6144, 18432),      # 64-row tiles, 2 row tiles, 512 whole + 64 x 4
+    "all_chunks_2": (48, 2048, 2048),               # 32 tiles < CUs: every tile in 2 chunks
+    "all_chunks_4": (64, 4096, 1536),               # 24 tiles: every tile in 4 chunks
+}
+
+
+@pytest.mark.parametrize("name", list(DENSE_SPLIT_CASES))
+@pytest.mark.timeout(600)
+def test_dense_decode_k_split(name):
+    T, D, F = DENSE_SPLIT_CASES[name]
+    w = wl.WORKLOADS["glm_decode"].with_(name=f"dense_split_{name}", T=T, D=D, seed=61,
+                                         weight_seed=61)
+    t0 = time.time()
+    dw = wl.make_dense(w, F)
+    x = wl.make_x(w)
+    out = run_dense(w, to_device(x), dw)
+    o = parity.compare_output(out, oracle.dense_ffn(x, *dw))
+    log(f"dense K split {name} (T={T}, D={D}, F={F}): max/rms={o.max_rel:.3e} "
+        f"mean/rms={o.mean_rel:.3e} ({time.time() - t0:.1f}s)")
+    assert_close(o, "bf16", f"dense K split {name}")
+    again = run_dense(w, to_device(x), dw)
+    assert np.array_equal(out, again), "dense K split is not deterministic"
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_dense_glm_width():
