@@ -71,12 +71,13 @@ int ksplit_for(int tiles, int ksteps, int per_cu) {
 }
 
 // Gate/up K split of the dense layer on a decode-size batch.  With `slots`
-// = 256 CUs x `per_cu` workgroups, the first whole * slots tiles (column-tile
-// major, `mt` row tiles per column) run whole, and the rest, rounded up to
-// whole columns of tiles, run in *ks K chunks so that every slot gets one
-// chunk: ks the largest divisor of the K steps with rest * ks <= slots and
-// chunks of at least 8 steps.  Every CU then streams about the same number
-// of K steps.  With fewer tiles than slots all run in chunks (ksplit_for).
+// = 256 CUs x `per_cu` workgroups and the tiles listed column-tile major
+// (`mt` row tiles per column): the last tiles % slots tiles, rounded up to
+// whole columns, run in *ks K chunks and the others (*whole) run whole, ks
+// the largest divisor of the K steps with (tiles - *whole) * ks <= slots and
+// chunks of at least 8 steps, so every slot gets at most one chunk and every
+// CU streams about the same number of K steps.  With fewer tiles than slots
+// every tile runs in chunks (ksplit_for); without a remainder none does.
 void plan_gateup_split(int tiles, int mt, int ksteps, int per_cu, int* whole, int* ks) {
   const int slots = 256 * (per_cu > 0 ? per_cu : 1);
   *whole = tiles;
