@@ -55,7 +55,9 @@ def measured_traffic(kind):
 def measured_peaks(torch):
     """Hardware ceilings measured on this GPU before the layer runs
     (libglm_peaks.so): bf16 and fp8 MFMA loops with the shader clock each
-    observed, and a streaming read of 8 GiB (far above the last-level cache)."""
+    observed, the 256 x 256 prefill tile's K step with its operands in L2
+    (MFMAs only, copies only, both with the fragment reads), and a streaming
+    read of 8 GiB (far above the last-level cache)."""
     import ctypes
     L = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_transformer_glm_amd", "libglm_peaks.so"))
     vp, i32, f32p, f64p = (ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
@@ -63,7 +65,7 @@ def measured_peaks(torch):
     L.glm_peak_mfma.argtypes = [i32, i32, i32, vp, f32p, f64p, f64p, vp]
     L.glm_peak_hbm_read.argtypes = [vp, ctypes.c_size_t, i32, vp, f32p, vp]
     stream = torch.cuda.current_stream().cuda_stream
-    scratch = torch.empty(16 + 4096 * 256 * 4, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(16 + 4096 * 512 * 4, dtype=torch.uint8, device="cuda")
     res = {}
     for name, fp8 in (("bf16", 0), ("fp8", 1)):
         ms, flops, mhz = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
@@ -73,6 +75,22 @@ def measured_peaks(torch):
             raise RuntimeError(f"glm_peak_mfma({name}) failed: hipError {st}")
         res[f"mfma_{name}_tflops"] = round(flops.value / (ms.value * 1e-3) / 1e12, 1)
         res[f"mfma_{name}_clock_mhz"] = round(mhz.value, 0)
+    # the 256 x 256 prefill tile's K step with its operands in L2
+    L.glm_peak_gemm_step.argtypes = [i32, i32, vp, vp, f64p, f64p, vp]
+    src = torch.ones(512 * 12288 // 2, dtype=torch.bfloat16, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    step = {}
+    for name, mode in (("mfma_only", 0), ("copies_only", 1), ("full", 2)):
+        us, mhz = ctypes.c_double(), ctypes.c_double()
+        st = L.glm_peak_gemm_step(mode, 4000, src.data_ptr(), scratch.data_ptr(),
+                                  ctypes.byref(us), ctypes.byref(mhz), stream)
+        if st != 0:
+            raise RuntimeError(f"glm_peak_gemm_step({name}) failed: hipError {st}")
+        step[name] = {"us_per_step": round(us.value, 4), "clock_mhz": round(mhz.value, 0)}
+    step["full_tflops"] = round(2.0 * 256 * 256 * 64 * cus / (step["full"]["us_per_step"] * 1e-6)
+                                / 1e12, 1)
+    res["gemm_step_l2"] = step
+    del src
     nbytes = 8 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     ms = ctypes.c_float()

@@ -42,6 +42,21 @@ int glm_peak_mfma(int fp8, int iters, int blocks_per_cu, void* scratch, float* m
 int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, float* ms,
                       hipStream_t stream);
 
+/* The K step of the 256 x 256 bf16 prefill tile with its operands in L2.  One
+ * 8-wave workgroup per compute unit runs `iters` (even, > 0) steps of `mode`:
+ * 0, the 32 v_mfma_f32_32x32x16_bf16 per wave only; 1, only the step's 64 KB
+ * of 16-byte LDS-DMA copies (256 activation and 256 weight rows, 128 bytes
+ * each) with the wait and the workgroup barrier of each step; 2, copies,
+ * LDS fragment reads and MFMAs, as the grouped GEMM's main loop does them on
+ * two 64 KB stages.  The copies read rows 12 KB apart from `src` (device
+ * buffer of at least 512 * 12288 bytes; 2 KB of each row, about 1 MB in all,
+ * so they hit L2).  Outputs (host pointers): *us_per_step, the timed launch
+ * over `iters` (HIP events); *clock_mhz, the shader clock one wave observed.
+ * `scratch`: caller-owned device buffer of at least
+ * 16 + 4 * 512 * (number of compute units) bytes. */
+int glm_peak_gemm_step(int mode, int iters, const void* src, void* scratch, double* us_per_step,
+                       double* clock_mhz, hipStream_t stream);
+
 /* Shader clock while other work runs.  Launches one wave on `stream` (do not
  * wait for it) that, every `period_us` microseconds for `seconds` (0 < seconds
  * <= 10) or until `max_samples` samples, stores the pair (shader clock

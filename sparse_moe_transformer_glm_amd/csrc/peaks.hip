@@ -11,6 +11,12 @@
 //  * HBM read: a streaming read of a buffer far larger than the last-level
 //    cache (16-byte non-temporal loads, many workgroups per CU so enough
 //    requests are in flight; the fastest of two launch shapes).
+//  * GEMM step: the K step of the 256 x 256 bf16 prefill tile with its data in
+//    L2 (one 8-wave workgroup per CU, two 64 KB LDS stages filled by 16-byte
+//    LDS-DMA copies, a wait and a barrier per step, 32 MFMAs per wave on
+//    fragments read from LDS), and the same step with only its MFMAs or only
+//    its copies: the time the tile design needs per step when no operand
+//    comes from HBM.
 //
 // Separate library (libglm_peaks.so): measurement only, not part of the layer.
 #include <hip/hip_runtime.h>
@@ -147,6 +153,107 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long tick
   if (threadIdx.x == 0) out[2 * max_samples] = (unsigned long long)n;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kStepRows = 512;      // A and B rows of a stage (256 + 256)
+constexpr int kStepK = 64;          // bf16 elements per row and step (128 bytes)
+constexpr int kStepRowStride = 6144;  // elements between rows of the source (12 KB)
+constexpr int kStepKCycle = 16;     // K steps before the source offset wraps (2 KB per row)
+// s_waitcnt immediate: vmcnt(0), no wait on expcnt and lgkmcnt
+constexpr int kVmcnt0 = (7 << 4) | (0xF << 8);
+
+__device__ inline int step_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// MODE 0: MFMAs only; 1: copies only; 2: copies, fragment reads and MFMAs.
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restrict__ src,
+                                                        int iters, float* sink,
+                                                        unsigned long long* clocks) {
+  constexpr int NW = 8, WN = 4, FM = 4, FN = 2, TM = 128, TN = 64, CP = 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t S0[kStepRows * kStepK];
+  __shared__ __attribute__((aligned(1024))) uint16_t S1[kStepRows * kStepK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kStepRows * kStepK; i += 512) {
+    S0[i] = (uint16_t)(0x3f80 + (i & 15));
+    S1[i] = (uint16_t)(0x3f00 + (i & 7));
+  }
+  __syncthreads();
+  // copy i of wave w: stage rows (w + 8 i) * 8 .. +8; lane l fills chunk l % 8
+  const uint16_t* s[CP];
+#pragma unroll
+  for (int i = 0; i < CP; ++i) {
+    const int r = (wave + NW * i) * 8 + lane / 8;
+    s[i] = src + (size_t)r * kStepRowStride + ((lane % 8) ^ step_swz(r)) * 8;
+  }
+  auto issue = [&](uint16_t* st, int kt) {
+#pragma unroll
+    for (int i = 0; i < CP; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(s[i] + (kt % kStepKCycle) * kStepK),
+                                       (lds_void*)(st + (wave + NW * i) * (8 * kStepK)), 16, 0,
+                                       0);
+  };
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane % 32, lk = lane / 32, sw = step_swz(lr);
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int m = 0; m < FM; ++m)
+#pragma unroll
+    for (int n = 0; n < FN; ++n) acc[m][n] = f32x16{};
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto load = [&](const uint16_t* st, int sub, int sl) {
+    const int off = ((2 * sub + lk) ^ sw) * 8;
+    const uint16_t* pa = st + (wm * TM + lr) * kStepK + off;
+    const uint16_t* pb = st + (256 + wn * TN + lr) * kStepK + off;
+#pragma unroll
+    for (int n = 0; n < FN; ++n) fb[sl][n] = *reinterpret_cast<const bf16x8*>(pb + n * 32 * kStepK);
+#pragma unroll
+    for (int m = 0; m < FM; ++m) fa[sl][m] = *reinterpret_cast<const bf16x8*>(pa + m * 32 * kStepK);
+  };
+  if (MODE != 0) issue(S0, 0);
+  load(S0, 0, 0);
+  load(S0, 1, 1);
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int kt = 0; kt < iters; kt += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint16_t* cur = h ? S1 : S0;
+      uint16_t* nxt = h ? S0 : S1;
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's copies of this step
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (MODE != 0) issue(nxt, kt + h + 1);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        if (MODE == 2) load(cur, (sub + 1) & 3, (sub + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (MODE != 1) {
+#pragma unroll
+          for (int m = 0; m < FM; ++m)
+#pragma unroll
+            for (int n = 0; n < FN; ++n)
+              acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub & 1][m], fb[sub & 1][n],
+                                                                  acc[m][n], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int m = 0; m < FM; ++m)
+#pragma unroll
+    for (int n = 0; n < FN; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += acc[m][n][i];
+  sum += (float)S0[tid * 8] + (float)S1[tid * 8];
+  if (sum == 1.2345e30f) sink[blockIdx.x * 512 + tid] = sum;  // keeps the work
+  if (blockIdx.x == 0 && tid == 0) {
+    clocks[0] = t1 - t0;
+    clocks[1] = r1 - r0;
+  }
+}
+
 int num_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -249,4 +356,47 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
   clock_probe_kernel<<<1, 64, 0, stream>>>(ticks, (unsigned long long)period_us * 100,
                                            max_samples, static_cast<unsigned long long*>(buf));
   return hipGetLastError();
+}
+
+// The K step of the 256 x 256 bf16 prefill tile with its operands in L2: one
+// 8-wave workgroup per CU runs `iters` steps (even) of `mode` (0: the 32
+// MFMAs per wave only; 1: only the 64 KB of LDS-DMA copies per workgroup,
+// with the wait and barrier of each step; 2: copies, fragment reads and
+// MFMAs).  The copies read rows 12 KB apart from `src`, a device buffer of at
+// least 512 * 12288 bytes, 2 KB of each (about 1 MB, L2-resident).  Writes
+// the time per step (*us_per_step, HIP events) and the shader clock one wave
+// observed (*clock_mhz).  `scratch`: device buffer of at least
+// 16 + 4 * 512 * (number of compute units) bytes.  Blocks until done.
+GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void* scratch,
+                                     double* us_per_step, double* clock_mhz, hipStream_t stream) {
+  const int cus = num_cus();
+  if (cus <= 0 || mode < 0 || mode > 2 || iters <= 0 || iters % 2 || !src || !scratch ||
+      !us_per_step || !clock_mhz)
+    return hipErrorInvalidValue;
+  unsigned long long* clocks = static_cast<unsigned long long*>(scratch);
+  float* sink = reinterpret_cast<float*>(clocks + 2);
+  const uint16_t* p = static_cast<const uint16_t*>(src);
+  auto launch = [&](int n) {
+    if (mode == 0) gemm_step_kernel<0><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else if (mode == 1) gemm_step_kernel<1><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else gemm_step_kernel<2><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+  };
+  hipEvent_t e0, e1;
+  hipError_t r;
+  if ((r = hipEventCreate(&e0)) != hipSuccess) return r;
+  if ((r = hipEventCreate(&e1)) != hipSuccess) return r;
+  launch(200);  // warm-up
+  (void)hipEventRecord(e0, stream);
+  launch(iters);
+  (void)hipEventRecord(e1, stream);
+  float ms = 0.f;
+  if ((r = hipEventSynchronize(e1)) == hipSuccess) r = hipEventElapsedTime(&ms, e0, e1);
+  unsigned long long host_clocks[2] = {0, 0};
+  if (r == hipSuccess) r = hipMemcpy(host_clocks, clocks, sizeof host_clocks, hipMemcpyDeviceToHost);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (r != hipSuccess) return r;
+  *us_per_step = ms * 1e3 / iters;
+  *clock_mhz = host_clocks[1] ? 100.0 * (double)host_clocks[0] / (double)host_clocks[1] : 0.0;
+  return hipSuccess;
 }

@@ -60,7 +60,8 @@ def test_peaks_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "glm_peaks.h")).read(),
                   flags=re.S)
     declared = sorted(set(re.findall(r"\b(glm_peak_\w+)\s*\(", text)))
-    assert declared == ["glm_peak_clock_probe", "glm_peak_hbm_read", "glm_peak_mfma"]
+    assert declared == ["glm_peak_clock_probe", "glm_peak_gemm_step", "glm_peak_hbm_read",
+                        "glm_peak_mfma"]
     out = subprocess.run(["nm", "-D", "--defined-only", B.PEAKS_LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (glm_\w+)", out))
