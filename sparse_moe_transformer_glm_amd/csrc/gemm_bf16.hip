@@ -523,6 +523,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
                          s_asg, s_wt);
 }
 
+#ifndef GLM_SPREAD_B  // spread the weight copies over the sub-steps (split rings)
+#define GLM_SPREAD_B 1
+#endif
+#ifndef GLM_SPREAD_PARTS  // ... over this many of them, the first ones
+#define GLM_SPREAD_PARTS 4
+#endif
+#ifndef GLM_SPREAD_MID  // ... each after its sub-step's first row block of MFMAs
+#define GLM_SPREAD_MID 1
+#endif
 // Split rings for the 256 x 256 prefill tiles.  The A rows (token
 // activations or hidden rows: each is re-read by every column tile of its
 // group, so mostly L2 hits) and the B rows (weights: streamed from HBM by the
@@ -531,9 +540,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
 // a wave waits for step kt+1, meets the workgroup barrier and refills the
 // slots step kt used with the A rows of step kt+2 and the B rows of step
 // kt+3, so the weight rows run two K steps ahead of the math with one
-// barrier per step.  Each slot is its own LDS object, so the compiler tracks
-// the LDS-DMA copies per slot.  Rows are 128-byte pieces (K step 64): a
-// narrower step would issue two requests per cache line.
+// barrier per step.  (With GLM_SPREAD_B the B rows of step kt+2 are issued
+// during step kt instead, one copy per sub-step after that sub-step's first
+// row block of MFMAs, into the slot step kt-1 left.)  Each slot is its own
+// LDS object, so the compiler tracks the LDS-DMA copies per slot.  Rows are
+// 128-byte pieces (K step 64): a narrower step would issue two requests per
+// cache line.
 template <class C, int MODE, int NA, int NB>
 __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownArgs dn) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MB = C::MB;
@@ -643,6 +655,21 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
       __builtin_amdgcn_global_load_lds((const void*)(sb[i] + (size_t)kt * BK),
                                        (lds_void*)(st + (wave + i * NW) * (RPI * BK)), 16, 0, 0);
   };
+  // SPREAD: the B copies of step kt+NB-1 are issued during step kt, BW/KSUB
+  // per sub-step, instead of all at the hand-over: a wave then never stalls
+  // on a burst of copies while its MFMAs wait to issue.
+  constexpr int PARTS = GLM_SPREAD_PARTS < C::KSUB ? GLM_SPREAD_PARTS : C::KSUB;
+  constexpr bool SPREAD = GLM_SPREAD_B && NA < NB && BW % PARTS == 0;
+  auto issueB_part = [&](bf16_t* st, int kt, int part) {
+    constexpr int BPS = BW / PARTS;
+    if (part >= PARTS) return;
+#pragma unroll
+    for (int j = 0; j < BPS; ++j) {
+      const int i = part * BPS + j;
+      __builtin_amdgcn_global_load_lds((const void*)(sb[i] + (size_t)kt * BK),
+                                       (lds_void*)(st + (wave + i * NW) * (RPI * BK)), 16, 0, 0);
+    }
+  };
 
   const int nk = K / BK;
   // The shallower ring's copies of a step are issued before the deeper
@@ -653,7 +680,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   auto issue_step = [&](auto live_c, int st) {  // the copies of step st in the prologue
     if (A_FIRST) {
       if (st < NA) issueA(live_c, a_slot(st), st);
-      if (st < NB) issueB(b_slot(st), st);
+      if (st < (SPREAD ? NB - 1 : NB)) issueB(b_slot(st), st);  // (SPREAD: step 0 copies B of NB-1)
     } else {
       if (st < NB) issueB(b_slot(st), st);
       if (st < NA) issueA(live_c, a_slot(st), st);
@@ -667,7 +694,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     if (nk > 2) {
       issue_step(live_c, 2);
       __builtin_amdgcn_s_waitcnt(
-          GLM_VMCNT(AWL + BW + (NA > 2 ? AWL : 0) + (NB > 2 ? BW : 0)));
+          GLM_VMCNT(AWL + BW + (NA > 2 ? AWL : 0) + (NB > 2 && !SPREAD ? BW : 0)));
     } else {
       __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     }
@@ -685,7 +712,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
     lds_barrier();
     if (A_FIRST) {
       if (STEADY || kt + NA < nk) issueA(live_c, a_slot(u % NA), kt + NA);
-      if (STEADY || kt + NB < nk) issueB(b_slot(u % NB), kt + NB);
+      if (!SPREAD && (STEADY || kt + NB < nk)) issueB(b_slot(u % NB), kt + NB);
     } else {
       if (STEADY || kt + NB < nk) issueB(b_slot(u % NB), kt + NB);
       if (STEADY || kt + NA < nk) issueA(live_c, a_slot(u % NA), kt + NA);
@@ -717,14 +744,17 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
       for (int m = 0; m < LIVE; ++m)
         fa[slot][m] = *reinterpret_cast<const bf16x8*>(pa + m * MB * BK);
     };
-    auto mma = [&](int slot) {
+    // MFMAs of row blocks [m0, m1) of a sub-step
+    auto mma_rows = [&](int slot, int m0, int m1) {
 #pragma unroll
       for (int m = 0; m < LIVE; ++m)
 #pragma unroll
         for (int n = 0; n < FN; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][m], fb[slot][n],
-                                                              acc[m][n], 0, 0, 0);
+          if (m >= m0 && m < m1)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][m], fb[slot][n],
+                                                                acc[m][n], 0, 0, 0);
     };
+    auto mma = [&](int slot) { mma_rows(slot, 0, LIVE); };
     prologue(live_c);
     load_frags(a_slot(0), b_slot(0), 0, 0);
     // one K step on the slots of step kt (u = kt % 6); the hand-over sits
@@ -737,13 +767,27 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
 #pragma unroll
       for (int sub = 0; sub < C::KSUB; ++sub) {
         if (sub + 1 < C::KSUB) load_frags(ca, cb, sub + 1, (sub + 1) & 1);
+        // (the last sub-step's part before the hand-over: its wait counts
+        // these as the youngest copies; the others after the first row
+        // block's MFMAs, so the MFMA pipe is busy while the copies issue)
+        const bool part = SPREAD && (STEADY || kt + NB - 1 < nk);
+        const bool mid = GLM_SPREAD_MID && sub + 1 < C::KSUB && LIVE > 1;
+        if (part && !mid) issueB_part(b_slot((u + NB - 1) % NB), kt + NB - 1, sub);
         if (sub == C::KSUB - 1 && (STEADY || kt + 1 < nk)) {
           handover(live_c, sc, kt, steady_c);
           load_frags(a_slot((u + 1) % NA), b_slot((u + 1) % NB), 0, 0);
         }
         // keep the reads issued above ahead of this sub-step's MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        mma(sub & 1);
+        if (mid) {
+          mma_rows(sub & 1, 0, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (part) issueB_part(b_slot((u + NB - 1) % NB), kt + NB - 1, sub);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_rows(sub & 1, 1, LIVE);
+        } else {
+          mma(sub & 1);
+        }
       }
     };
     int kt = 0;
@@ -765,12 +809,16 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
       const std::integral_constant<int, 0> none{};
       prologue(none);
       int kt = 0;
+      auto idle_step = [&](auto uc, int k) {  // step k of a wave row without MFMA work
+        constexpr int u = decltype(uc)::value;
+        if (SPREAD && k + NB - 1 < nk) issueB(b_slot((u + NB - 1) % NB), k + NB - 1);
+        handover(none, uc, k, std::false_type{});
+      };
       for (; kt + 6 < nk; kt += 6)
-        unroll<6>([&](auto uc) { handover(none, uc, kt + decltype(uc)::value, std::false_type{}); });
+        unroll<6>([&](auto uc) { idle_step(uc, kt + decltype(uc)::value); });
       for (; kt + 1 < nk; kt += 6)
         unroll<6>([&](auto uc) {
-          if (kt + decltype(uc)::value + 1 < nk)
-            handover(none, uc, kt + decltype(uc)::value, std::false_type{});
+          if (kt + decltype(uc)::value + 1 < nk) idle_step(uc, kt + decltype(uc)::value);
         });
     }
   }
