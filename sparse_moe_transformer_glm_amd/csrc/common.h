@@ -54,6 +54,9 @@ constexpr int kXcdBlockDecodeDn = GLM_XCD_BLOCK_DECODE_DN;
 #ifndef GLM_EARLY_MAX_ROWS
 #define GLM_EARLY_MAX_ROWS 160.0
 #endif
+#ifndef GLM_ZIP  // rounds of the longest-first lists zipped (zip_position):
+#define GLM_ZIP 3  // bit 0 gate/up list, bit 1 down list
+#endif
 
 // Cache policy of the weight-row copies.  The only row tile of a group is the
 // only reader of the group's weight rows in a launch, so on decode tiles (at
@@ -134,6 +137,9 @@ struct ScanParams {
   // order run whole, the others in gu_ksplit K chunks each; gu_shared_n is
   // the number of descriptors (whole tiles plus chunks)
   int gu_ksplit, gu_whole, gu_shared_n;
+  // XCD block (xcd_tile) of each launch whose longest-first list is zipped
+  // round by round (zip_position), 0: listing order
+  int gu_zip, dn_zip;
 };
 hipError_t launch_scan(const uint64_t* masks, const ScanParams& p,
                        int32_t* counts, int32_t* offsets, int32_t* tile_base,
@@ -307,6 +313,27 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Physical place of logical position i of a list of n tiles listed longest
+// first and cut into units of `unit` tiles (the last, partial unit keeps its
+// place): of the nb full units, logical unit b goes to unit 2b when
+// b < ceil(nb / 2) and to unit 2 (nb - 1 - b) + 1 otherwise, so the heaviest
+// and the lightest units alternate.  A permutation of [0, n).
+__host__ __device__ inline int zip_position(int i, int n, int unit) {
+  if (unit <= 0) return i;
+  const int nb = n / unit, b = i / unit;
+  if (b >= nb) return i;
+  const int half = (nb + 1) / 2;
+  const int pb = b < half ? 2 * b : 2 * (nb - 1 - b) + 1;
+  return pb * unit + i % unit;
+}
+// One dispatch round of xcd_tile over a list of n tiles with XCD block xb:
+// a block of consecutive tiles for each XCD (0: no zipping).
+__host__ __device__ inline int xcd_round(int n, int xb) {
+  if (n <= 0 || xb <= 0) return 0;
+  const int rounds = cdiv(n, kXcds * xb);
+  return kXcds * cdiv(n, kXcds * rounds);
+}
 
 // Workgroup -> logical tile of a grouped GEMM launch.  Workgroups are
 // dispatched round-robin over the XCDs (workgroup b on XCD b % 8).  The n

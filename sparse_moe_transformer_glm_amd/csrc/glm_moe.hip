@@ -387,6 +387,11 @@ int run_experts(const Plan& P, const void* x, const void* xin, int32_t* idx, flo
   sp.gu_ksplit = P.gu_ksplit;
   sp.gu_whole = P.gu_whole;
   sp.gu_shared_n = P.gu_shared_n;
+  // routed bf16 layers: the longest-first lists are zipped by dispatch rounds
+  // (the XCD blocks below), so each XCD alternates heavy and light rounds
+  const bool zip = P.bf16 && !P.mx && !P.dense;
+  sp.gu_zip = zip && (GLM_ZIP & 1) ? (P.gu.BM == 256 ? kXcdBlockRoutedGu : kXcdBlock) : 0;
+  sp.dn_zip = zip && (GLM_ZIP & 2) ? (P.dn.BM == 32 ? kXcdBlockDecodeDn : kXcdBlock) : 0;
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCAN));
   GLM_HIP(launch_scan(masks, sp, counts, offsets, tile_base, gu_desc, gu_count, dn_desc, dn_count, s));
   GLM_HIP(rec.mark(GLM_MOE_STAGE_SCATTER));

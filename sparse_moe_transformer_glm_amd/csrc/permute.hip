@@ -58,10 +58,11 @@ __device__ inline int tile_row0(int m, int mt, int rows, int gran) {
 // previous round's last position, a few LDS reads per round.
 __device__ inline void write_descs(const int* pos, const int* og, int total, const int* cnt,
                                    const int* off, int T, int E, int BM, int shared_nt,
-                                   int col_w, int ksplit, int whole,
+                                   int col_w, int ksplit, int whole, int zip_xb,
                                    TileDesc* __restrict__ out) {
   constexpr int kWaves = kScanThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int unit = xcd_round(zip_xb > 0 ? total : 0, zip_xb);  // tiles per zipped unit
   const int chunk = cdiv(cdiv(total, kWaves), kWave) * kWave;
   const int b0 = wave * chunk, b1 = min(total, b0 + chunk);
   if (b0 >= b1) return;
@@ -114,7 +115,7 @@ __device__ inline void write_descs(const int* pos, const int* og, int total, con
     d.row0 = (g < E ? off[g] : 0) + r0;
     d.rows = rt;
     d.col0 = nt * col_w;
-    out[i] = d;
+    out[zip_position(i, total, unit)] = d;
   }
 }
 
@@ -299,9 +300,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
   // tile descriptors: groups in listing order, then output-column tile, then row tile
   write_descs(s_pg, s_og, s_gu[E + 1], s_cnt, s_off, p.T, E, p.gu.BM, 2 * p.Fs / p.gu.BN,
-              p.gu.BN / 2, p.gu_ksplit, p.gu_ksplit > 1 ? p.gu_whole : -1, gu_desc);
+              p.gu.BN / 2, p.gu_ksplit, p.gu_ksplit > 1 ? p.gu_whole : -1,
+              lpt_g ? p.gu_zip : 0, gu_desc);
   write_descs(s_pd, s_od, s_dn[E + 1], s_cnt, s_off, p.T, E, p.dn.BM, p.D / p.dn.BN, p.dn.BN,
-              p.dn_ksplit, -1, dn_desc);
+              p.dn_ksplit, -1, lpt_d ? p.dn_zip : 0, dn_desc);
 }
 
 // One wave per 64-token tile.  A token's rank among the tile's tokens of
