@@ -602,18 +602,19 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
   const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
 
-  // A copies: wave (wm, wn) fills rows wn*RPI .. +RPI of each MFMA row block
-  // of its wave row, so it makes exactly one A copy per live block and rows
-  // of blocks past the valid rows are never fetched (the LDS rows they would
-  // fill reach only output rows that the epilogue drops).  B copy i of a wave
-  // covers rows (wave + i*NW)*RPI .. +RPI.  Lane l fills physical chunk
-  // l % CPR of its row, logical chunk (l % CPR) ^ swz.
-  static_assert(C::WN * RPI == MB, "the waves of a wave row cover one row block per copy");
-  const bf16_t* sa[FM];
-  int a_dst[FM];
+  // A copies: copy c of wave (wm, wn) fills rows (c*WN + wn)*RPI .. +RPI of
+  // each MFMA row block of its wave row, so it makes exactly CPB A copies per
+  // live block and rows of blocks past the valid rows are never fetched (the
+  // LDS rows they would fill reach only output rows that the epilogue drops).
+  // B copy i of a wave covers rows (wave + i*NW)*RPI .. +RPI.  Lane l fills
+  // physical chunk l % CPR of its row, logical chunk (l % CPR) ^ swz.
+  constexpr int CPB = MB / (WN * RPI);  // A copies per live block per wave
+  static_assert(CPB >= 1 && CPB * WN * RPI == MB, "a wave row's copies cover whole row blocks");
+  const bf16_t* sa[FM * CPB];
+  int a_dst[FM * CPB];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    a_dst[i] = min(wrow0 + i * MB, BM - MB) + wn * RPI;
+  for (int i = 0; i < FM * CPB; ++i) {
+    a_dst[i] = min(wrow0 + (i / CPB) * MB, BM - MB) + ((i % CPB) * WN + wn) * RPI;
     const int r = a_dst[i] + lane / CPR;
     sa[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff +
             ((lane % CPR) ^ swz<BK>(r)) * 8;
@@ -641,11 +642,11 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   };
   auto a_slot = [&](int s) -> bf16_t* { return slot(s); };
   auto b_slot = [&](int s) -> bf16_t* { return slot(NA + s); };
-  // LIVE: the wave row's live blocks (compile time), the wave's A copies per step
+  // LIVE: the wave row's live blocks (compile time); the wave makes LIVE * CPB A copies a step
   auto issueA = [&](auto live_c, bf16_t* st, int kt) {
     constexpr int LIVE = decltype(live_c)::value;
 #pragma unroll
-    for (int i = 0; i < LIVE; ++i)
+    for (int i = 0; i < LIVE * CPB; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(sa[i] + (size_t)kt * BK),
                                        (lds_void*)(st + a_dst[i] * BK), 16, 0, 0);
   };
@@ -688,7 +689,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   };
   // Steps 0 .. NMAX-1 in step order; wait for step 0
   auto prologue = [&](auto live_c) {
-    constexpr int AWL = decltype(live_c)::value;
+    constexpr int AWL = decltype(live_c)::value * CPB;  // A copies per step
     issue_step(live_c, 0);
     if (nk > 1) issue_step(live_c, 1);
     if (nk > 2) {
@@ -706,7 +707,7 @@ __global__ __launch_bounds__(C::NT) void split_gemm_kernel(GateUpArgs gu, DownAr
   auto handover = [&](auto live_c, auto sc, int kt, auto steady_c) {
     constexpr int u = decltype(sc)::value;  // kt % 6
     constexpr bool STEADY = decltype(steady_c)::value;
-    constexpr int DEEP_W = A_FIRST ? BW : decltype(live_c)::value;
+    constexpr int DEEP_W = A_FIRST ? BW : decltype(live_c)::value * CPB;
     if (STEADY || kt + 2 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(DEEP_W));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
