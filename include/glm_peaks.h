@@ -48,7 +48,10 @@ int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, fl
  * of 16-byte LDS-DMA copies (256 activation and 256 weight rows, 128 bytes
  * each) with the wait and the workgroup barrier of each step; 2, copies,
  * LDS fragment reads and MFMAs, as the grouped GEMM's main loop does them on
- * two 64 KB stages.  The copies read rows 12 KB apart from `src` (device
+ * two 64 KB stages, each wave issuing its 8 copies of the next step at the
+ * hand-over; 3, as 2 with each wave's copies spread over the step, two after
+ * each of the 4 sub-steps' first row block of MFMAs (the way the prefill
+ * kernel issues its weight copies).  The copies read rows 12 KB apart from `src` (device
  * buffer of at least 512 * 12288 bytes; 2 KB of each row, about 1 MB in all,
  * so they hit L2).  Outputs (host pointers): *us_per_step, the timed launch
  * over `iters` (HIP events); *clock_mhz, the shader clock one wave observed.

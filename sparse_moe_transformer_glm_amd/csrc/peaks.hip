@@ -163,7 +163,10 @@ constexpr int kVmcnt0 = (7 << 4) | (0xF << 8);
 
 __device__ inline int step_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// MODE 0: MFMAs only; 1: copies only; 2: copies, fragment reads and MFMAs.
+// MODE 0: MFMAs only; 1: copies only; 2: copies, fragment reads and MFMAs;
+// 3: as 2 with each wave's copies of the next step spread over the step, two
+// after each sub-step's first row block of MFMAs, instead of all at the
+// hand-over.
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restrict__ src,
                                                         int iters, float* sink,
@@ -184,13 +187,16 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
     const int r = (wave + NW * i) * 8 + lane / 8;
     s[i] = src + (size_t)r * kStepRowStride + ((lane % 8) ^ step_swz(r)) * 8;
   }
-  auto issue = [&](uint16_t* st, int kt) {
+  // copies [i0, i1) of this wave for step kt into stage st
+  auto issue_range = [&](uint16_t* st, int kt, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < CP; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(s[i] + (kt % kStepKCycle) * kStepK),
-                                       (lds_void*)(st + (wave + NW * i) * (8 * kStepK)), 16, 0,
-                                       0);
+      if (i >= i0 && i < i1)
+        __builtin_amdgcn_global_load_lds((const void*)(s[i] + (kt % kStepKCycle) * kStepK),
+                                         (lds_void*)(st + (wave + NW * i) * (8 * kStepK)), 16, 0,
+                                         0);
   };
+  auto issue = [&](uint16_t* st, int kt) { issue_range(st, kt, 0, CP); };
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % 32, lk = lane / 32, sw = step_swz(lr);
   f32x16 acc[FM][FN];
@@ -220,18 +226,24 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
       uint16_t* nxt = h ? S0 : S1;
       __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's copies of this step
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (MODE != 0) issue(nxt, kt + h + 1);
+      if (MODE == 1 || MODE == 2) issue(nxt, kt + h + 1);
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        if (MODE == 2) load(cur, (sub + 1) & 3, (sub + 1) & 1);
+        if (MODE >= 2) load(cur, (sub + 1) & 3, (sub + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
         if (MODE != 1) {
 #pragma unroll
-          for (int m = 0; m < FM; ++m)
+          for (int m = 0; m < FM; ++m) {
 #pragma unroll
             for (int n = 0; n < FN; ++n)
               acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub & 1][m], fb[sub & 1][n],
                                                                   acc[m][n], 0, 0, 0);
+            if (MODE == 3 && m == 0) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue_range(nxt, kt + h + 1, sub * (CP / 4), (sub + 1) * (CP / 4));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         }
       }
     }
@@ -362,7 +374,8 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
 // 8-wave workgroup per CU runs `iters` steps (even) of `mode` (0: the 32
 // MFMAs per wave only; 1: only the 64 KB of LDS-DMA copies per workgroup,
 // with the wait and barrier of each step; 2: copies, fragment reads and
-// MFMAs).  The copies read rows 12 KB apart from `src`, a device buffer of at
+// MFMAs; 3: as 2 with each wave's copies spread over the step, two after
+// each sub-step's first row block of MFMAs).  The copies read rows 12 KB apart from `src`, a device buffer of at
 // least 512 * 12288 bytes, 2 KB of each (about 1 MB, L2-resident).  Writes
 // the time per step (*us_per_step, HIP events) and the shader clock one wave
 // observed (*clock_mhz).  `scratch`: device buffer of at least
@@ -370,7 +383,7 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
 GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void* scratch,
                                      double* us_per_step, double* clock_mhz, hipStream_t stream) {
   const int cus = num_cus();
-  if (cus <= 0 || mode < 0 || mode > 2 || iters <= 0 || iters % 2 || !src || !scratch ||
+  if (cus <= 0 || mode < 0 || mode > 3 || iters <= 0 || iters % 2 || !src || !scratch ||
       !us_per_step || !clock_mhz)
     return hipErrorInvalidValue;
   unsigned long long* clocks = static_cast<unsigned long long*>(scratch);
@@ -379,7 +392,8 @@ GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void*
   auto launch = [&](int n) {
     if (mode == 0) gemm_step_kernel<0><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
     else if (mode == 1) gemm_step_kernel<1><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
-    else gemm_step_kernel<2><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else if (mode == 2) gemm_step_kernel<2><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else gemm_step_kernel<3><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
   };
   hipEvent_t e0, e1;
   hipError_t r;
