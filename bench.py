@@ -56,10 +56,11 @@ def measured_peaks(torch):
     """Hardware ceilings measured on this GPU before the layer runs
     (libglm_peaks.so): bf16 and fp8 MFMA loops with the shader clock each
     observed, the 256 x 256 prefill tile's K step with its operands in L2
-    (MFMAs only, copies only, both with the fragment reads, and both with
-    the copies spread over the step as the prefill kernel issues its weight
-    copies), and a streaming read of 8 GiB (far above the last-level
-    cache)."""
+    (MFMAs only, copies only, both with the fragment reads, both with the
+    copies spread over the step as the prefill kernel issues its weight
+    copies, copies and MFMAs without the reads, reads and MFMAs without the
+    copies; each also in shader-clock cycles), and a streaming read of 8 GiB
+    (far above the last-level cache)."""
     import ctypes
     L = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_transformer_glm_amd", "libglm_peaks.so"))
     vp, i32, f32p, f64p = (ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
@@ -82,13 +83,15 @@ def measured_peaks(torch):
     src = torch.ones(512 * 12288 // 2, dtype=torch.bfloat16, device="cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     step = {}
-    for name, mode in (("mfma_only", 0), ("copies_only", 1), ("full", 2), ("full_spread", 3)):
+    for name, mode in (("mfma_only", 0), ("copies_only", 1), ("full", 2), ("full_spread", 3),
+                       ("copies_mfma", 4), ("reads_mfma", 5)):
         us, mhz = ctypes.c_double(), ctypes.c_double()
         st = L.glm_peak_gemm_step(mode, 4000, src.data_ptr(), scratch.data_ptr(),
                                   ctypes.byref(us), ctypes.byref(mhz), stream)
         if st != 0:
             raise RuntimeError(f"glm_peak_gemm_step({name}) failed: hipError {st}")
-        step[name] = {"us_per_step": round(us.value, 4), "clock_mhz": round(mhz.value, 0)}
+        step[name] = {"us_per_step": round(us.value, 4), "clock_mhz": round(mhz.value, 0),
+                      "cycles_per_step": round(us.value * mhz.value, 0)}
     for name in ("full", "full_spread"):
         step[f"{name}_tflops"] = round(2.0 * 256 * 256 * 64 * cus
                                        / (step[name]["us_per_step"] * 1e-6) / 1e12, 1)

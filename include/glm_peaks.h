@@ -51,7 +51,9 @@ int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, fl
  * two 64 KB stages, each wave issuing its 8 copies of the next step at the
  * hand-over; 3, as 2 with each wave's copies spread over the step, two after
  * each of the 4 sub-steps' first row block of MFMAs (the way the prefill
- * kernel issues its weight copies).  The copies read rows 12 KB apart from `src` (device
+ * kernel issues its weight copies); 4, as 3 without the fragment reads
+ * (copies and MFMAs only); 5, fragment reads and MFMAs without copies.
+ * The copies read rows 12 KB apart from `src` (device
  * buffer of at least 512 * 12288 bytes; 2 KB of each row, about 1 MB in all,
  * so they hit L2).  Outputs (host pointers): *us_per_step, the timed launch
  * over `iters` (HIP events); *clock_mhz, the shader clock one wave observed.

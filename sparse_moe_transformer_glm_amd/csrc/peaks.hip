@@ -166,7 +166,8 @@ __device__ inline int step_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // MODE 0: MFMAs only; 1: copies only; 2: copies, fragment reads and MFMAs;
 // 3: as 2 with each wave's copies of the next step spread over the step, two
 // after each sub-step's first row block of MFMAs, instead of all at the
-// hand-over.
+// hand-over; 4: as 3 without the fragment reads (copies and MFMAs); 5:
+// fragment reads and MFMAs, no copies.
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restrict__ src,
                                                         int iters, float* sink,
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
 #pragma unroll
     for (int m = 0; m < FM; ++m) fa[sl][m] = *reinterpret_cast<const bf16x8*>(pa + m * 32 * kStepK);
   };
-  if (MODE != 0) issue(S0, 0);
+  if (MODE != 0 && MODE != 5) issue(S0, 0);
   load(S0, 0, 0);
   load(S0, 1, 1);
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
       if (MODE == 1 || MODE == 2) issue(nxt, kt + h + 1);
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        if (MODE >= 2) load(cur, (sub + 1) & 3, (sub + 1) & 1);
+        if (MODE == 2 || MODE == 3 || MODE == 5) load(cur, (sub + 1) & 3, (sub + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
         if (MODE != 1) {
 #pragma unroll
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
             for (int n = 0; n < FN; ++n)
               acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub & 1][m], fb[sub & 1][n],
                                                                   acc[m][n], 0, 0, 0);
-            if (MODE == 3 && m == 0) {
+            if ((MODE == 3 || MODE == 4) && m == 0) {
               __builtin_amdgcn_sched_barrier(0);
               issue_range(nxt, kt + h + 1, sub * (CP / 4), (sub + 1) * (CP / 4));
               __builtin_amdgcn_sched_barrier(0);
@@ -375,7 +376,8 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
 // MFMAs per wave only; 1: only the 64 KB of LDS-DMA copies per workgroup,
 // with the wait and barrier of each step; 2: copies, fragment reads and
 // MFMAs; 3: as 2 with each wave's copies spread over the step, two after
-// each sub-step's first row block of MFMAs).  The copies read rows 12 KB apart from `src`, a device buffer of at
+// each sub-step's first row block of MFMAs; 4: as 3 without the fragment
+// reads; 5: fragment reads and MFMAs without copies).  The copies read rows 12 KB apart from `src`, a device buffer of at
 // least 512 * 12288 bytes, 2 KB of each (about 1 MB, L2-resident).  Writes
 // the time per step (*us_per_step, HIP events) and the shader clock one wave
 // observed (*clock_mhz).  `scratch`: device buffer of at least
@@ -383,7 +385,7 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
 GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void* scratch,
                                      double* us_per_step, double* clock_mhz, hipStream_t stream) {
   const int cus = num_cus();
-  if (cus <= 0 || mode < 0 || mode > 3 || iters <= 0 || iters % 2 || !src || !scratch ||
+  if (cus <= 0 || mode < 0 || mode > 5 || iters <= 0 || iters % 2 || !src || !scratch ||
       !us_per_step || !clock_mhz)
     return hipErrorInvalidValue;
   unsigned long long* clocks = static_cast<unsigned long long*>(scratch);
@@ -393,7 +395,9 @@ GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void*
     if (mode == 0) gemm_step_kernel<0><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
     else if (mode == 1) gemm_step_kernel<1><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
     else if (mode == 2) gemm_step_kernel<2><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
-    else gemm_step_kernel<3><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else if (mode == 3) gemm_step_kernel<3><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else if (mode == 4) gemm_step_kernel<4><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else gemm_step_kernel<5><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
   };
   hipEvent_t e0, e1;
   hipError_t r;
