@@ -59,7 +59,8 @@ def measured_peaks(torch):
     (MFMAs only, copies only, both with the fragment reads, both with the
     copies spread over the step as the prefill kernel issues its weight
     copies, copies and MFMAs without the reads, reads and MFMAs without the
-    copies; each also in shader-clock cycles), and a streaming read of 8 GiB
+    copies, MFMAs with the copies moved through registers; each also in
+    shader-clock cycles), and a streaming read of 8 GiB
     (far above the last-level cache)."""
     import ctypes
     L = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_transformer_glm_amd", "libglm_peaks.so"))
@@ -84,7 +85,7 @@ def measured_peaks(torch):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     step = {}
     for name, mode in (("mfma_only", 0), ("copies_only", 1), ("full", 2), ("full_spread", 3),
-                       ("copies_mfma", 4), ("reads_mfma", 5)):
+                       ("copies_mfma", 4), ("reads_mfma", 5), ("regcopies_mfma", 6)):
         us, mhz = ctypes.c_double(), ctypes.c_double()
         st = L.glm_peak_gemm_step(mode, 4000, src.data_ptr(), scratch.data_ptr(),
                                   ctypes.byref(us), ctypes.byref(mhz), stream)

@@ -52,7 +52,10 @@ int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, fl
  * hand-over; 3, as 2 with each wave's copies spread over the step, two after
  * each of the 4 sub-steps' first row block of MFMAs (the way the prefill
  * kernel issues its weight copies); 4, as 3 without the fragment reads
- * (copies and MFMAs only); 5, fragment reads and MFMAs without copies.
+ * (copies and MFMAs only); 5, fragment reads and MFMAs without copies; 6,
+ * MFMAs with the same rows moved through registers (16-byte loads of the next
+ * step after the barrier, LDS writes after the step's MFMAs), no fragment
+ * reads.
  * The copies read rows 12 KB apart from `src` (device
  * buffer of at least 512 * 12288 bytes; 2 KB of each row, about 1 MB in all,
  * so they hit L2).  Outputs (host pointers): *us_per_step, the timed launch

@@ -167,7 +167,9 @@ __device__ inline int step_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // 3: as 2 with each wave's copies of the next step spread over the step, two
 // after each sub-step's first row block of MFMAs, instead of all at the
 // hand-over; 4: as 3 without the fragment reads (copies and MFMAs); 5:
-// fragment reads and MFMAs, no copies.
+// fragment reads and MFMAs, no copies; 6: MFMAs with the step's 64 KB moved
+// through registers instead (16-byte loads of the next step after the
+// barrier, LDS writes after the MFMAs), no fragment reads.
 template <int MODE>
 __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restrict__ src,
                                                         int iters, float* sink,
@@ -198,6 +200,18 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
                                          0);
   };
   auto issue = [&](uint16_t* st, int kt) { issue_range(st, kt, 0, CP); };
+  // MODE 6: the same rows through registers
+  u32x4 stg[CP];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CP; ++i)
+      stg[i] = *reinterpret_cast<const u32x4*>(s[i] + (kt % kStepKCycle) * kStepK);
+  };
+  auto lwrite = [&](uint16_t* st) {
+#pragma unroll
+    for (int i = 0; i < CP; ++i)
+      *reinterpret_cast<u32x4*>(st + (wave + NW * i) * (8 * kStepK) + lane * 8) = stg[i];
+  };
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % 32, lk = lane / 32, sw = step_swz(lr);
   f32x16 acc[FM][FN];
@@ -215,7 +229,11 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
 #pragma unroll
     for (int m = 0; m < FM; ++m) fa[sl][m] = *reinterpret_cast<const bf16x8*>(pa + m * 32 * kStepK);
   };
-  if (MODE != 0 && MODE != 5) issue(S0, 0);
+  if (MODE != 0 && MODE != 5 && MODE != 6) issue(S0, 0);
+  if (MODE == 6) {
+    gload(0);
+    lwrite(S0);
+  }
   load(S0, 0, 0);
   load(S0, 1, 1);
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
@@ -228,6 +246,7 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
       __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's copies of this step
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (MODE == 1 || MODE == 2) issue(nxt, kt + h + 1);
+      if (MODE == 6) gload(kt + h + 1);
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         if (MODE == 2 || MODE == 3 || MODE == 5) load(cur, (sub + 1) & 3, (sub + 1) & 1);
@@ -246,6 +265,10 @@ __global__ __launch_bounds__(512) void gemm_step_kernel(const uint16_t* __restri
             }
           }
         }
+      }
+      if (MODE == 6) {
+        __builtin_amdgcn_sched_barrier(0);
+        lwrite(nxt);
       }
     }
   }
@@ -377,7 +400,9 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
 // with the wait and barrier of each step; 2: copies, fragment reads and
 // MFMAs; 3: as 2 with each wave's copies spread over the step, two after
 // each sub-step's first row block of MFMAs; 4: as 3 without the fragment
-// reads; 5: fragment reads and MFMAs without copies).  The copies read rows 12 KB apart from `src`, a device buffer of at
+// reads; 5: fragment reads and MFMAs without copies; 6: MFMAs with the
+// rows moved through registers, 16-byte loads then LDS writes, no fragment
+// reads).  The copies read rows 12 KB apart from `src`, a device buffer of at
 // least 512 * 12288 bytes, 2 KB of each (about 1 MB, L2-resident).  Writes
 // the time per step (*us_per_step, HIP events) and the shader clock one wave
 // observed (*clock_mhz).  `scratch`: device buffer of at least
@@ -385,7 +410,7 @@ GLM_PEAKS_API int glm_peak_clock_probe(double seconds, int period_us, int max_sa
 GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void* scratch,
                                      double* us_per_step, double* clock_mhz, hipStream_t stream) {
   const int cus = num_cus();
-  if (cus <= 0 || mode < 0 || mode > 5 || iters <= 0 || iters % 2 || !src || !scratch ||
+  if (cus <= 0 || mode < 0 || mode > 6 || iters <= 0 || iters % 2 || !src || !scratch ||
       !us_per_step || !clock_mhz)
     return hipErrorInvalidValue;
   unsigned long long* clocks = static_cast<unsigned long long*>(scratch);
@@ -397,7 +422,8 @@ GLM_PEAKS_API int glm_peak_gemm_step(int mode, int iters, const void* src, void*
     else if (mode == 2) gemm_step_kernel<2><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
     else if (mode == 3) gemm_step_kernel<3><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
     else if (mode == 4) gemm_step_kernel<4><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
-    else gemm_step_kernel<5><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else if (mode == 5) gemm_step_kernel<5><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
+    else gemm_step_kernel<6><<<cus, 512, 0, stream>>>(p, n, sink, clocks);
   };
   hipEvent_t e0, e1;
   hipError_t r;
