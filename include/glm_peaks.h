@@ -1,10 +1,11 @@
 /* Measured hardware ceilings of the GPU (libglm_peaks.so).
  *
- * Not part of the MoE layer: two microbenchmarks whose rates the benchmark
+ * Not part of the MoE layer: microbenchmarks whose rates the benchmark
  * reports beside the published MI355X peaks, so that each kernel's roofline
  * fraction can also be read against what the chip sustains at the clock it
- * actually ran.  Both run on the calling thread's current HIP device, on
- * `stream`, and block until their timed launches have finished.
+ * actually ran, and a shader-clock sampler.  All run on the calling thread's
+ * current HIP device, on `stream`; all but the clock sampler block until
+ * their timed launches have finished.
  *
  * Return value: a hipError_t value, 0 on success; hipErrorInvalidValue (1)
  * for a null pointer, a non-positive count or a misaligned size.
@@ -55,8 +56,7 @@ int glm_peak_hbm_read(const void* src, size_t bytes, int reps, void* scratch, fl
  * (copies and MFMAs only); 5, fragment reads and MFMAs without copies; 6,
  * MFMAs with the same rows moved through registers (16-byte loads of the next
  * step after the barrier, LDS writes after the step's MFMAs), no fragment
- * reads.
- * The copies read rows 12 KB apart from `src` (device
+ * reads.  The copies read rows 12 KB apart from `src` (device
  * buffer of at least 512 * 12288 bytes; 2 KB of each row, about 1 MB in all,
  * so they hit L2).  Outputs (host pointers): *us_per_step, the timed launch
  * over `iters` (HIP events); *clock_mhz, the shader clock one wave observed.
