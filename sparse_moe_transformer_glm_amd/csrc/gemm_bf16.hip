@@ -263,6 +263,9 @@ __device__ __forceinline__ void tile_epilogue(const GateUpArgs& gu, const DownAr
 
 // EARLY (two stages only): each stage's refill is issued before the wait for
 // the next stage instead of after it (see the main loop).
+#ifndef GLM_LIVE_A  // uniform-ring kernel: copy only the live row blocks' A rows
+#define GLM_LIVE_A 1
+#endif
 template <class C, int MODE, bool EARLY>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, DownArgs dn) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, ST = C::ST, MB = C::MB;
@@ -313,6 +316,13 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     }
   }
 
+  // MFMA row blocks holding valid rows, dealt to the wave rows in turn as
+  // evenly as possible: a SIMD runs one wave of each wave row, so its MFMA
+  // work is the blocks of both (ceil(rows / MB) in all, not WM x the larger)
+  const int nb = (rows + MB - 1) / MB;
+  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
+  const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
+
   // DMA sources: instruction q = wave + i*NW covers rows [q*RPI, q*RPI+RPI) of
   // the stage (A rows first, then B rows); lane l fills physical chunk l % CPR
   // of row q*RPI + l / CPR, i.e. logical chunk (l % CPR) ^ swz(row).
@@ -323,6 +333,31 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     const int r = q * RPI + lane / CPR;
     const int ch = (lane % CPR) ^ swz<BK>(r);
     src[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff + ch * 8;
+  }
+  // LIVEA (the waves of a wave row cover one row block per copy): instead,
+  // wave (wm, wn) copies rows wn*RPI .. +RPI of each live row block of its
+  // wave row, LIVE A copies a stage, so rows of blocks past the valid rows
+  // are never fetched (their LDS rows reach no MFMA), and BW weight-row
+  // copies: B copy i covers B rows (wave + i*NW)*RPI .. +RPI.
+  constexpr bool LIVEA = GLM_LIVE_A && C::WN * RPI == MB && C::B_INST % NW == 0;
+  constexpr int BW = C::B_INST / NW;
+  const bf16_t* sa_l[LIVEA ? FM : 1];
+  int a_dst[LIVEA ? FM : 1];
+  const bf16_t* sb_l[LIVEA ? BW : 1];
+  if constexpr (LIVEA) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      a_dst[i] = min(wrow0 + i * MB, BM - MB) + wn * RPI;
+      const int r = a_dst[i] + lane / CPR;
+      sa_l[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff +
+                ((lane % CPR) ^ swz<BK>(r)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < BW; ++i) {
+      const int r = BM + (wave + i * NW) * RPI + lane / CPR;
+      sb_l[i] = tile_row_src<MODE, BM, MB>(gu, dn, g, row0, rows, col0, r) + koff +
+                ((lane % CPR) ^ swz<BK>(r)) * 8;
+    }
   }
 
   // Per-row data of the down epilogue (assignment and routing weight of row
@@ -360,12 +395,25 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     }
   };
 
-  // MFMA row blocks holding valid rows, dealt to the wave rows in turn as
-  // evenly as possible: a SIMD runs one wave of each wave row, so its MFMA
-  // work is the blocks of both (ceil(rows / MB) in all, not WM x the larger)
-  const int nb = (rows + MB - 1) / MB;
-  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
-  const int wrow0 = MB * (wm * (nb / C::WM) + min(wm, nb % C::WM));
+  // copies of step kt into stage st: LIVE A copies and BW B copies (LIVEA),
+  // else the IPW uniform copies
+  auto issue_any = [&](bf16_t* st, int kt, auto nt_c, auto live_c) {
+    if constexpr (LIVEA) {
+      constexpr bool NT = decltype(nt_c)::value;
+      constexpr int LIVE = decltype(live_c)::value;
+#pragma unroll
+      for (int i = 0; i < LIVE; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(sa_l[i] + (size_t)kt * BK),
+                                         (lds_void*)(st + a_dst[i] * BK), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BW; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(sb_l[i] + (size_t)kt * BK),
+                                         (lds_void*)(st + (BM + (wave + i * NW) * RPI) * BK),
+                                         16, 0, NT ? kCpolNt : 0);
+    } else {
+      issue(st, kt, nt_c);
+    }
+  };
 
   // fragment read offsets (elements, without the stage base and k-chunk)
   const int lr = lane % MB, lk = lane / MB;
@@ -389,6 +437,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
   // before the last sub-step's MFMAs.
   auto run = [&](auto live_c, auto nt_c) {
     constexpr int LIVE = decltype(live_c)::value;
+    constexpr int VPS = LIVEA ? LIVE + BW : IPW;  // this wave's copies per stage
     bf16x8 fa[2][FM], fb[2][FN];
     auto load_frags = [&](const bf16_t* st, int sub, int slot) {
       const int kc = (MB == 32 ? 2 * sub : 4 * sub) + lk;  // logical 16-byte chunk
@@ -418,8 +467,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
     // prologue: fill every stage, wait for stage 0, read its first fragments
 #pragma unroll
     for (int s = 0; s < ST; ++s)
-      if (s < nk) issue(stage_ptr(s), s, nt_c);
-    if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 1)));
+      if (s < nk) issue_any(stage_ptr(s), s, nt_c, live_c);
+    if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS * (ST - 1)));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
     load_frags(stage_ptr(0), 0, 0);
@@ -442,17 +491,17 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
             // every wave that all copies of stage kt+1 have landed.
             lds_barrier();  // every wave is done reading stage kt
             if (kt + 2 < nk) {
-              issue(cur, kt + 2, nt_c);
-              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW));  // this wave's copies of kt+1
+              issue_any(cur, kt + 2, nt_c, live_c);
+              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS));  // this wave's copies of kt+1
             } else {
               __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
             }
             asm volatile("s_barrier" ::: "memory");
           } else {
-            if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW * (ST - 2)));
+            if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS * (ST - 2)));
             else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
             lds_barrier();
-            if (kt + ST < nk) issue(cur, kt + ST, nt_c);
+            if (kt + ST < nk) issue_any(cur, kt + ST, nt_c, live_c);
           }
           load_frags(stage_ptr((s + 1) % ST), 0, 0);  // slot 0 is free: sub-step KSUB-2 used it
         }
@@ -479,17 +528,20 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
       case 3: if constexpr (FM >= 3) run(std::integral_constant<int, 3>{}, nt_c); break;
       case 4: if constexpr (FM >= 4) run(std::integral_constant<int, 4>{}, nt_c); break;
       default: {
-        // this wave row holds no valid row: keep the barrier count of the others
+        // this wave row holds no valid row: make its copies (LIVEA: weight
+        // rows only) and keep the barrier count of the others
+        const std::integral_constant<int, 0> none{};
+        constexpr int VPS0 = LIVEA ? BW : IPW;
         for (int s = 0; s < ST; ++s)
-          if (s < nk) issue(stage_ptr(s), s, nt_c);
+          if (s < nk) issue_any(stage_ptr(s), s, nt_c, none);
         __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
         lds_barrier();
         for (int kt = 0; kt + 1 < nk; ++kt) {
           if constexpr (early) {  // the same two barriers per step as the other waves
             lds_barrier();
             if (kt + 2 < nk) {
-              issue(stage_ptr(kt % ST), kt + 2, nt_c);
-              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(IPW));
+              issue_any(stage_ptr(kt % ST), kt + 2, nt_c, none);
+              __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS0));
             } else {
               __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
             }
@@ -497,7 +549,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GateUpArgs gu, Down
           } else {
             __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
             lds_barrier();
-            if (kt + ST < nk) issue(stage_ptr(kt % ST), kt + ST, nt_c);
+            if (kt + ST < nk) issue_any(stage_ptr(kt % ST), kt + ST, nt_c, none);
           }
         }
       }
