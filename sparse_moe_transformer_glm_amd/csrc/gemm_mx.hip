@@ -48,6 +48,9 @@ constexpr int BK = 128;   // K elements (bytes) per stage
 constexpr int KSUB = 2;   // 64-element MFMA steps per stage
 constexpr int CPR = 8;    // 16-byte chunks per row
 constexpr int RPI = 8;    // rows per 1 KB DMA instruction
+#ifndef GLM_MX_LIVE_A  // copy only the live row blocks' activation rows
+#define GLM_MX_LIVE_A 1
+#endif
 
 template <int BM_, int BN_, int WM_, int WN_, int ST_>
 struct Cfg {
@@ -230,6 +233,45 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     }
   }
 
+  // 32-row MFMA blocks holding valid rows, dealt to the wave rows as evenly
+  // as possible (a SIMD runs one wave of each wave row)
+  const int nb = (rows + 31) / 32;
+  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
+  const int wrow0 = 32 * (wm * (nb / C::WM) + min(wm, nb % C::WM));
+
+  // LIVEA: instead of the uniform data copies above, copy c of wave (wm, wn)
+  // fills rows (c*WN + wn)*RPI .. +RPI of each live row block of its wave row
+  // (CPB copies a block), so rows of blocks past the valid rows are never
+  // fetched (their LDS rows reach no MFMA); B copy i covers B rows
+  // (wave + i*NW)*RPI .. +RPI.  The scale copies stay as above.
+  constexpr int CPB = 32 / (WN * RPI) > 0 ? 32 / (WN * RPI) : 1;
+  constexpr bool LIVEA = GLM_MX_LIVE_A && CPB * WN * RPI == 32 && C::B_INST % NW == 0;
+  constexpr int BW = C::B_INST / NW;
+  const uint8_t* sa_l[LIVEA ? FM * CPB : 1];
+  int a_dst[LIVEA ? FM * CPB : 1];
+  const uint8_t* sb_l[LIVEA ? BW : 1];
+  if constexpr (LIVEA) {
+#pragma unroll
+    for (int i = 0; i < FM * CPB; ++i) {
+      a_dst[i] = min(wrow0 + (i / CPB) * 32, BM - 32) + ((i % CPB) * WN + wn) * RPI;
+      const int r = a_dst[i] + lane / CPR;
+      const uint8_t* d;
+      const uint8_t* sc;
+      size_t step;
+      a_row(r, &d, &sc, &step);
+      sa_l[i] = d + ((lane % CPR) ^ swz(r)) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < BW; ++i) {
+      const int n = (wave + i * NW) * RPI + lane / CPR;
+      const uint8_t* d;
+      const uint8_t* sc;
+      size_t step;
+      b_row(n, &d, &sc, &step);
+      sb_l[i] = d + ((lane % CPR) ^ swz(BM + n)) * 16;
+    }
+  }
+
   // Per-row data of the down epilogue, loaded into registers here and written
   // to LDS at the epilogue (the loads stay off the path to the first K step).
   static_assert(BM <= C::NT, "one epilogue row per thread");
@@ -264,13 +306,29 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
       __builtin_amdgcn_global_load_lds((const void*)(ssrc[i] + (size_t)kt * sstep[i]),
                                        (lds_void*)(st + sdst[i]), 4, 0, 0);
   };
-  constexpr int VPS = IPW + SPW;  // DMA instructions per wave per stage
-
-  // 32-row MFMA blocks holding valid rows, dealt to the wave rows as evenly
-  // as possible (a SIMD runs one wave of each wave row)
-  const int nb = (rows + 31) / 32;
-  const int live_m = min(FM, nb / C::WM + (wm < nb % C::WM ? 1 : 0));
-  const int wrow0 = 32 * (wm * (nb / C::WM) + min(wm, nb % C::WM));
+  // copies of step kt into stage st: LIVE * CPB A copies, BW B copies and the
+  // scale copies (LIVEA), else the uniform ones
+  auto issue_any = [&](uint8_t* st, int kt, auto nt_c, auto live_c) {
+    if constexpr (LIVEA) {
+      constexpr bool NT = decltype(nt_c)::value;
+      constexpr int LIVE = decltype(live_c)::value;
+#pragma unroll
+      for (int i = 0; i < LIVE * CPB; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(sa_l[i] + (size_t)kt * BK),
+                                         (lds_void*)(st + a_dst[i] * BK), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BW; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(sb_l[i] + (size_t)kt * BK),
+                                         (lds_void*)(st + (BM + (wave + i * NW) * RPI) * BK),
+                                         16, 0, NT ? kCpolNt : 0);
+#pragma unroll
+      for (int i = 0; i < SPW; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc[i] + (size_t)kt * sstep[i]),
+                                         (lds_void*)(st + sdst[i]), 4, 0, 0);
+    } else {
+      issue(st, kt, nt_c);
+    }
+  };
 
   const int lr = lane % 32, lg = lane / 32;
   const int sw = swz(lr);
@@ -296,6 +354,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
 
   auto run = [&](auto live_c, auto nt_c) {
     constexpr int LIVE = decltype(live_c)::value;
+    constexpr int VPS = LIVEA ? LIVE * CPB + BW + SPW : IPW + SPW;  // copies per wave and stage
     i32x8 fa[LIVE > 0 ? LIVE : 1], fb[FN];
     uint32_t sa[LIVE > 0 ? LIVE : 1], sb[FN];
     auto frag = [&](const uint8_t* st, int lo_off, int hi_off) -> i32x8 {
@@ -330,7 +389,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
     };
 #pragma unroll
     for (int s = 0; s < ST; ++s)
-      if (s < nk) issue(stage_ptr(s), s, nt_c);
+      if (s < nk) issue_any(stage_ptr(s), s, nt_c, live_c);
     if (ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS * (ST - 1)));
     else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
     lds_barrier();
@@ -348,7 +407,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_mx_kernel(MxGateUpArgs gu,
           if (kt + ST - 1 < nk) __builtin_amdgcn_s_waitcnt(GLM_VMCNT(VPS * (ST - 2)));
           else __builtin_amdgcn_s_waitcnt(GLM_VMCNT(0));
           lds_barrier();
-          if (kt + ST < nk) issue(cur, kt + ST, nt_c);
+          if (kt + ST < nk) issue_any(cur, kt + ST, nt_c, live_c);
         }
         if constexpr (LIVE > 0) mma(sub);
         // keep the next sub-step's fragment reads behind these MFMAs: one
